@@ -1,0 +1,248 @@
+"""Plain, slow, fp64 CPU oracle for single-token decode attention over a paged KV cache.
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU-baseline leg of
+the benchmark may import this module. The product path (the HIP library and its Python
+binding) never imports it, and this module imports nothing from the product path.
+
+Sources (the pages this follows, cited by page title and section):
+
+* "LLM 推理优化全景实战" (chenxutan.com), §2.3 "PagedAttention 的实现细节": the block pool
+  is shaped [num_blocks, block_size, num_heads, head_dim]; a request's page table maps
+  logical block -> physical block; a token at index t lives in logical block
+  t // block_size at offset t % block_size (write_kv / read_kv).
+* same page, §2.4 "PagedAttention 的注意力计算": gather the request's blocks through the
+  page table, score = q . k / sqrt(head_dim), softmax over tokens, output = weights . V.
+* "09-inference-optimization" (LLM-Code-Hot-100), section "KV Cache": the new token's
+  K/V is written into the cache *before* attention, the scale is 1/sqrt(head_dim), and
+  the per-layer cache size is 2 * batch * kv_heads * seq * head_dim * dtype_bytes;
+  section "PagedAttention": only the used slots of a page are part of the sequence
+  (get_kv slices each page to its used slots).
+* "LLM推理与服务：面试问题与推荐回答", Q7: grouped-query attention, G query heads share one
+  KV head; "推理机制动态图解（进阶）" demo 1 assigns query heads 0-15 with KV heads 0-3,
+  i.e. groups are contiguous: kv_head(h) = h // G.
+* "推理机制动态图解（进阶）" demo 5 "FlashAttention：分块与在线 softmax": running max m,
+  exponent sum l and unnormalised output O, rescaled by exp(m_old - m_new) whenever the
+  max grows; the final O / l equals the standard softmax result.
+
+What is computed here is the plain definition: gather every used slot through the table,
+score in fp64, two-pass softmax (subtract the maximum, exponentiate, normalise) and the
+fp64 weighted sum of V. The online / partitioned form in `online_softmax_attention`
+follows demo 5's steps and is kept to pin the reading that partition results merge by
+the same rescale rule; it is checked against the two-pass definition, not the other way
+round.
+
+Storage dtypes: "f32" (numpy float32), "f16" (numpy float16) and "bf16" (numpy uint16
+holding the upper 16 bits of an IEEE binary32, since numpy has no bfloat16).
+
+Every function here is pinned by a CPU test (closed forms, hand-worked values, a library
+attention routine, invariants); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+STORAGE_DTYPES = ("f32", "f16", "bf16")
+_NUMPY_STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def storage_to_f64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Decode stored elements to fp64 exactly.
+
+    bf16 is the upper half of an IEEE binary32: shifting the 16 stored bits into the
+    high half of a 32-bit word gives the binary32 value, which fp64 holds exactly.
+    """
+    if dtype == "bf16":
+        if arr.dtype != np.uint16:
+            raise TypeError("bf16 arrays are stored as uint16 bit patterns")
+        with np.errstate(invalid="ignore"):     # signalling-NaN patterns stay NaN
+            return (arr.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype not in ("f32", "f16"):
+        raise ValueError(f"unknown storage dtype {dtype!r}")
+    if arr.dtype != _NUMPY_STORAGE[dtype]:
+        raise TypeError(f"{dtype} arrays must be {_NUMPY_STORAGE[dtype].__name__}")
+    return arr.astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------
+# KV-cache size ("09-inference-optimization", section "KV Cache": the size formula and
+# analyze_kv_cache_memory; "LLM推理与服务：面试问题与推荐回答" Q1: ~0.5 MB per token).
+# --------------------------------------------------------------------------------------
+
+def kv_cache_bytes(n_layers: int, batch: int, seq_len: int, n_kv_heads: int,
+                   d_head: int, dtype_bytes: int) -> int:
+    """2 (K and V) x layers x batch x seq_len x kv_heads x head_dim x bytes per element."""
+    return 2 * n_layers * batch * seq_len * n_kv_heads * d_head * dtype_bytes
+
+
+def kv_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, dtype_bytes: int) -> int:
+    """Bytes one token adds to the cache across all layers: the formula at batch = seq = 1."""
+    return kv_cache_bytes(n_layers, 1, 1, n_kv_heads, d_head, dtype_bytes)
+
+
+# --------------------------------------------------------------------------------------
+# Append and read through the page table (chenxutan §2.3 write_kv / read_kv).
+# --------------------------------------------------------------------------------------
+
+def _slot(table_row: np.ndarray, token_idx: int, block_size: int) -> tuple[int, int]:
+    logical_block = token_idx // block_size
+    block_offset = token_idx % block_size
+    return int(table_row[logical_block]), block_offset
+
+
+def kv_append(k_pool: np.ndarray, v_pool: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+              block_tables: np.ndarray, positions: np.ndarray, block_size: int):
+    """Return copies of the pools with each sequence's new token written at its position.
+
+    k_pool, v_pool: [num_blocks, block_size, n_kv_heads, d_head] (stored dtype).
+    k_new, v_new:   [B, n_kv_heads, d_head] (same stored dtype).
+    positions[b]:   token index of the new token (the context length before the step).
+    The write is a plain element copy, so the result is exact in the stored dtype.
+    """
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    for b in range(k_new.shape[0]):
+        phys, off = _slot(block_tables[b], int(positions[b]), block_size)
+        k_out[phys, off] = k_new[b]
+        v_out[phys, off] = v_new[b]
+    return k_out, v_out
+
+
+def read_kv(pool: np.ndarray, table_row: np.ndarray, token_idx: int, block_size: int) -> np.ndarray:
+    """One token's [n_kv_heads, d_head] slice, found through the page table."""
+    phys, off = _slot(table_row, token_idx, block_size)
+    return pool[phys, off]
+
+
+def gather_kv(pool: np.ndarray, table_row: np.ndarray, n_tokens: int, block_size: int,
+              kv_head: int | None = None) -> np.ndarray:
+    """Tokens 0..n_tokens-1 of one sequence in logical order, stored dtype.
+
+    Returns [n_tokens, n_kv_heads, d_head], or [n_tokens, d_head] for one kv_head. Only
+    the used slots are read: slots at or past n_tokens are never touched. This is
+    read_kv applied to every token index, written as one indexed read.
+    """
+    t = np.arange(n_tokens, dtype=np.int64)
+    phys = np.asarray(table_row, dtype=np.int64)[t // block_size]
+    off = t % block_size
+    if kv_head is None:
+        return pool[phys, off]
+    return pool[phys, off, kv_head]
+
+
+# --------------------------------------------------------------------------------------
+# Decode attention, plain definition (chenxutan §2.4; "09-inference-optimization",
+# AttentionWithKVCache with a single query token, where no causal mask applies).
+# --------------------------------------------------------------------------------------
+
+def softmax_two_pass(scores: np.ndarray) -> np.ndarray:
+    """Numerically stable softmax over the last axis: exp(s - max) / sum(exp(s - max))."""
+    m = np.max(scores, axis=-1, keepdims=True)
+    e = np.exp(scores - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def paged_decode_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                           block_tables: np.ndarray, context_lens: np.ndarray,
+                           block_size: int, scale: float, dtype: str,
+                           pairs=None) -> np.ndarray:
+    """fp64 attention output for one query token per sequence.
+
+    q:            [B, n_heads, d_head] stored dtype.
+    k_pool/v_pool:[num_blocks, block_size, n_kv_heads, d_head] stored dtype, *after* the
+                  append (the new token is part of the context).
+    block_tables: [B, max_blocks_per_seq] int.
+    context_lens: [B] tokens attended, including the just-appended one (N_b >= 1).
+    pairs:        optional iterable of (b, h) to compute; other outputs stay NaN.
+    Returns [B, n_heads, d_head] fp64.
+    """
+    B, n_heads, d_head = q.shape
+    n_kv_heads = k_pool.shape[2]
+    if n_heads % n_kv_heads:
+        raise ValueError("n_heads must be a multiple of n_kv_heads")
+    group = n_heads // n_kv_heads
+    out = np.full((B, n_heads, d_head), np.nan, dtype=np.float64)
+
+    wanted = {}
+    if pairs is None:
+        for b in range(B):
+            for h in range(n_heads):
+                wanted.setdefault((b, h // group), []).append(h)
+    else:
+        for b, h in pairs:
+            wanted.setdefault((int(b), int(h) // group), []).append(int(h))
+
+    for (b, j) in sorted(wanted):
+        n_tok = int(context_lens[b])
+        if n_tok < 1:
+            raise ValueError("every sequence attends to at least its new token")
+        keys = storage_to_f64(gather_kv(k_pool, block_tables[b], n_tok, block_size, j), dtype)
+        vals = storage_to_f64(gather_kv(v_pool, block_tables[b], n_tok, block_size, j), dtype)
+        for h in sorted(set(wanted[(b, j)])):
+            qh = storage_to_f64(q[b, h], dtype)
+            scores = scale * (keys @ qh)            # [n_tok]
+            weights = softmax_two_pass(scores)      # [n_tok]
+            out[b, h] = weights @ vals              # [d_head]
+    return out
+
+
+# --------------------------------------------------------------------------------------
+# Online softmax over tiles and the merge of partition results ("推理机制动态图解（进阶）"
+# demo 5; the split of one sequence's KV over many workers is "Scaling Book 第 11 章"
+# §11.8 FlashDecoding). Kept in fp64 to pin the reading that partitions merge by the
+# rescale rule.
+# --------------------------------------------------------------------------------------
+
+def online_softmax_partial(q_vec: np.ndarray, keys: np.ndarray, vals: np.ndarray,
+                           scale: float, tile_tokens: int):
+    """Run demo 5's loop over consecutive tiles of keys/vals; return (m, l, O).
+
+    Start with m = -inf, l = 0, O = 0. For each tile: S = scale * q . K_tile; the new
+    maximum m_new = max(m, max S); the old l and O are multiplied by exp(m - m_new); the
+    tile adds sum exp(S - m_new) to l and exp(S - m_new) . V_tile to O. The caller
+    divides O by l (deferred normalisation).
+    """
+    m = -math.inf
+    l = 0.0
+    o = np.zeros(vals.shape[-1], dtype=np.float64)
+    for start in range(0, keys.shape[0], tile_tokens):
+        k_tile = keys[start:start + tile_tokens]
+        v_tile = vals[start:start + tile_tokens]
+        s = scale * (k_tile @ q_vec)
+        m_new = max(m, float(np.max(s)))
+        rescale = math.exp(m - m_new) if m != -math.inf else 0.0
+        p = np.exp(s - m_new)
+        l = l * rescale + float(np.sum(p))
+        o = o * rescale + p @ v_tile
+        m = m_new
+    return m, l, o
+
+
+def merge_partitions(ms, ls, os_):
+    """Combine partition results (m_p, l_p, O_p) into the attention output.
+
+    The same rescale rule as between tiles: m* = max m_p, each partition is weighted by
+    exp(m_p - m*), and the merged O is divided by the merged l. Partitions with no tokens
+    carry m = -inf, l = 0 and contribute nothing.
+    """
+    m_star = max(ms)
+    weights = [math.exp(m - m_star) if m != -math.inf else 0.0 for m in ms]
+    l_star = sum(w * l for w, l in zip(weights, ls))
+    o_star = sum(w * o for w, o in zip(weights, os_))
+    return o_star / l_star
+
+
+def online_softmax_attention(q_vec: np.ndarray, keys: np.ndarray, vals: np.ndarray,
+                             scale: float, tile_tokens: int = 16,
+                             partition_tokens: int | None = None) -> np.ndarray:
+    """fp64 output via tiles (and optional partitions merged by the rescale rule)."""
+    if partition_tokens is None:
+        m, l, o = online_softmax_partial(q_vec, keys, vals, scale, tile_tokens)
+        return o / l
+    parts = [online_softmax_partial(q_vec, keys[s:s + partition_tokens],
+                                    vals[s:s + partition_tokens], scale, tile_tokens)
+             for s in range(0, keys.shape[0], partition_tokens)]
+    return merge_partitions([p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts])
