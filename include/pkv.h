@@ -1,0 +1,187 @@
+/*
+ * pkv.h - C ABI of libpkv: single-token decode attention over a paged KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (sources cited by page title and section):
+ *
+ *   * "LLM 推理优化全景实战" (chenxutan.com) §2.3: K and V live in two pools shaped
+ *     [num_blocks, block_size, n_kv_heads, d_head]; each sequence owns a table that maps
+ *     its logical block i to a physical block; token t sits in logical block
+ *     t / block_size at slot t % block_size.
+ *   * same page §2.4: decode attention for one query token gathers the sequence's
+ *     blocks through its table, scores every cached token with q . k * scale, takes a
+ *     softmax over the tokens and returns the probability-weighted sum of the V rows.
+ *   * "09-inference-optimization" (LLM-Code-Hot-100), section "KV Cache": the new
+ *     token's K/V enters the cache before attention is computed, the scale is
+ *     1/sqrt(d_head), and a cache holds 2 * layers * batch * seq * kv_heads * d_head *
+ *     dtype_bytes bytes.
+ *   * "LLM推理与服务：面试问题与推荐回答" Q7 and "推理机制动态图解（进阶）" demo 1:
+ *     grouped-query attention; query head h reads KV head h / (n_heads / n_kv_heads).
+ *   * "推理机制动态图解（进阶）" demo 5: the softmax is taken online (running maximum,
+ *     running sum, rescale on a new maximum, divide at the end); "Scaling Book 第 11 章"
+ *     §11.8 (FlashDecoding): one long sequence is split over many compute units.
+ *
+ * Conventions shared by every entry point:
+ *
+ *   * Every pointer argument is DEVICE memory owned by the caller, except where stated.
+ *     The library allocates nothing, frees nothing, keeps no state between calls and
+ *     never synchronises: each call checks its arguments on the host, enqueues its
+ *     kernels on `stream` and returns.
+ *   * dtype is one of PKV_F32, PKV_F16, PKV_BF16; K, V, q, k_new, v_new and out share it.
+ *     Arithmetic is fp32 throughout (fp32 products and accumulation); outputs are
+ *     rounded to the dtype with round-to-nearest-even.
+ *   * Supported shapes: block_size == 16, d_head in {64, 128},
+ *     n_heads / n_kv_heads in {1, 2, 4, 8}. All device pointers must be 16-byte aligned.
+ *   * Return value: PKV_OK (0) or a negative PKV_ERR_* code. Errors are found on the
+ *     host before anything is enqueued (except PKV_ERR_LAUNCH). Device-side values
+ *     (tables, lengths, positions) are not read by the host; a kernel that meets an
+ *     out-of-range value never reads or writes out of bounds: kv_append skips that
+ *     sequence, gather_kv skips that block, and paged_decode_attention writes NaN to
+ *     every output of that sequence's affected heads.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pkv_dtype { PKV_F32 = 0, PKV_F16 = 1, PKV_BF16 = 2 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* a size is non-positive or sizes disagree */
+  PKV_ERR_DTYPE = -3,       /* dtype is not PKV_F32 / PKV_F16 / PKV_BF16 */
+  PKV_ERR_HEAD_DIM = -4,    /* d_head is not 64 or 128 */
+  PKV_ERR_BLOCK_SIZE = -5,  /* block_size is not 16 */
+  PKV_ERR_GROUP = -6,       /* n_heads is not n_kv_heads * {1, 2, 4, 8} */
+  PKV_ERR_CONTEXT = -7,     /* max_context_len < 1 or > max_blocks_per_seq * block_size */
+  PKV_ERR_PARTITION = -8,   /* partition_tokens is negative or not a multiple of block_size */
+  PKV_ERR_WORKSPACE = -9,   /* workspace is NULL or smaller than pkv_decode_workspace_bytes */
+  PKV_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch */
+  PKV_ERR_ALIGN = -11,      /* a device pointer is not 16-byte aligned */
+  PKV_ERR_ALIAS = -12       /* out overlaps q, k_pool or v_pool */
+};
+
+/*
+ * pkv_kv_append - write each sequence's new token into its slot of the pools.
+ *
+ * Source: chenxutan §2.3 (write_kv: logical block t / block_size, offset
+ * t % block_size, store K and V there); "09-inference-optimization" KV Cache (the write
+ * precedes attention).
+ *
+ *   k_pool, v_pool  [num_blocks, block_size, n_kv_heads, d_head], dtype; written in place.
+ *   k_new, v_new    [num_seqs, n_kv_heads, d_head], dtype; read only.
+ *   block_tables    [num_seqs, max_blocks_per_seq] int32, row-major; entry i of row b is
+ *                   the physical block holding sequence b's tokens 16*i .. 16*i+15.
+ *   positions       [num_seqs] int32; positions[b] is the token index of the new token,
+ *                   i.e. sequence b's context length before this step.
+ *
+ * The write is a byte copy (bit-exact). The table entry for the new token's block must
+ * already be allocated by the caller; a sequence whose position or table entry is out of
+ * range is skipped. Sequences must not share the slot they write (a shared block is
+ * copied by the caller's block manager before the write). Enqueue this before
+ * pkv_paged_decode_attention on the same stream so the new token is attended to.
+ */
+int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                      const int32_t* block_tables, const int32_t* positions,
+                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                      int32_t block_size, int32_t n_kv_heads, int32_t d_head, int32_t dtype,
+                      hipStream_t stream);
+
+/*
+ * pkv_paged_decode_attention - one query token per sequence attends to its paged
+ * context.
+ *
+ * Source: chenxutan §2.4 (gather through the page table, softmax(q K^T * scale) V);
+ * "推理机制动态图解（进阶）" demo 5 (online softmax with deferred division);
+ * "Scaling Book 第 11 章" §11.8 (split one sequence's KV across compute units).
+ *
+ *   out             [num_seqs, n_heads, d_head], dtype; written. Must not overlap q or
+ *                   the pools.
+ *   q               [num_seqs, n_heads, d_head], dtype.
+ *   k_pool, v_pool  [num_blocks, block_size, n_kv_heads, d_head], dtype.
+ *   block_tables    [num_seqs, max_blocks_per_seq] int32, row-major.
+ *   context_lens    [num_seqs] int32; context_lens[b] = N_b, the number of tokens sequence
+ *                   b attends to, INCLUDING the token just appended (1 <= N_b <=
+ *                   max_context_len). A sequence with N_b outside that range, or whose
+ *                   table holds an entry outside [0, num_blocks) among its first
+ *                   ceil(N_b / 16) entries, gets NaN outputs.
+ *   max_context_len host-side upper bound of context_lens; sizes the launch grid.
+ *   scale           score multiplier, normally 1/sqrt(d_head).
+ *   partition_tokens tokens per KV partition (a multiple of 16); 0 selects 512. A
+ *                   sequence longer than one partition is processed by several
+ *                   workgroups whose partial results a second kernel merges.
+ *   workspace       device scratch of at least pkv_decode_workspace_bytes(...) bytes
+ *                   (may be NULL when that size is 0); its contents on entry do not
+ *                   matter and on return are unspecified.
+ *
+ * Query head h uses KV head h / (n_heads / n_kv_heads). Results do not depend on the
+ * physical placement of blocks (bitwise), and are deterministic (no atomics).
+ */
+int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks,
+                                   int32_t max_context_len, int32_t block_size,
+                                   int32_t n_heads, int32_t n_kv_heads, int32_t d_head,
+                                   float scale, int32_t partition_tokens, int32_t dtype,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/*
+ * pkv_decode_workspace_bytes - scratch bytes pkv_paged_decode_attention needs (host
+ * only, no device call). 0 when every sequence fits one partition. Returns 0 for
+ * invalid sizes as well; pkv_paged_decode_attention then reports the invalid argument.
+ *
+ * Layout (fp32, 256-byte aligned sections): running maxima [num_seqs, n_heads, P],
+ * sums [num_seqs, n_heads, P], unnormalised outputs [num_seqs, n_heads, P, d_head], with
+ * P = ceil(max_context_len / partition_tokens).
+ */
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t d_head,
+                                  int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ * pkv_kv_bytes_per_token - bytes one token occupies in the KV cache of a whole model:
+ * 2 * n_layers * n_kv_heads * d_head * dtype_bytes (host only).
+ *
+ * Source: "09-inference-optimization" KV Cache (the size formula at batch = seq = 1);
+ * "LLM推理与服务：面试问题与推荐回答" Q1 (about 0.5 MB for 32 layers x 32 heads x 128, fp16).
+ * Returns -1 if an argument is negative.
+ */
+int64_t pkv_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_head,
+                               int32_t dtype_bytes);
+
+/*
+ * pkv_gather_kv - copy each sequence's cached tokens into contiguous arrays (test and
+ * inspection use; not on the decode path).
+ *
+ * Source: chenxutan §2.3 read_kv (the same slot rule as the append) and
+ * "09-inference-optimization" PagedAttention get_kv (only used slots).
+ *
+ *   k_out, v_out    [num_seqs, max_context_len, n_kv_heads, d_head], dtype; row t of
+ *                   sequence b is written for t < min(context_lens[b], max_context_len);
+ *                   the rest is left untouched.
+ * Other arguments as for pkv_paged_decode_attention. Blocks whose table entry is out of
+ * range are skipped. Bit-exact copy.
+ */
+int32_t pkv_gather_kv(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                      int32_t max_context_len, int32_t block_size, int32_t n_kv_heads,
+                      int32_t d_head, int32_t dtype, hipStream_t stream);
+
+/* pkv_status_str - static, NUL-terminated description of a status code (host only). */
+const char* pkv_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

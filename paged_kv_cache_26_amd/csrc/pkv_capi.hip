@@ -1,0 +1,213 @@
+// C ABI of libpkv: host-side argument checks, workspace sizing and kernel dispatch.
+// The operations and their sources are documented in include/pkv.h.
+
+#include "../../include/pkv.h"
+
+#include <cmath>
+
+#include "pkv_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int32_t elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_F16:
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool valid_group(int32_t n_heads, int32_t n_kv_heads) {
+  if (n_kv_heads <= 0 || n_heads <= 0 || n_heads % n_kv_heads) return false;
+  const int32_t g = n_heads / n_kv_heads;
+  return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+int32_t resolve_partition(int32_t partition_tokens) {
+  return partition_tokens == 0 ? pkv::kDefaultPartition : partition_tokens;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Byte ranges [a, a + na) and [b, b + nb) overlap.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Checks shared by decode and gather.
+int32_t check_pool_args(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        int32_t max_context_len, int32_t block_size, int32_t n_kv_heads,
+                        int32_t d_head, int32_t dtype) {
+  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
+  if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || n_kv_heads <= 0)
+    return PKV_ERR_SHAPE;
+  if (num_seqs > 65535) return PKV_ERR_SHAPE;   // grid z / y limit
+  if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return PKV_ERR_CONTEXT;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pkv_status_str(int32_t status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_SHAPE: return "a size is non-positive or sizes disagree";
+    case PKV_ERR_DTYPE: return "unsupported dtype (expected PKV_F32, PKV_F16 or PKV_BF16)";
+    case PKV_ERR_HEAD_DIM: return "unsupported d_head (expected 64 or 128)";
+    case PKV_ERR_BLOCK_SIZE: return "unsupported block_size (expected 16)";
+    case PKV_ERR_GROUP: return "n_heads must be n_kv_heads times 1, 2, 4 or 8";
+    case PKV_ERR_CONTEXT: return "max_context_len must be in [1, max_blocks_per_seq * block_size]";
+    case PKV_ERR_PARTITION: return "partition_tokens must be 0 or a positive multiple of block_size";
+    case PKV_ERR_WORKSPACE: return "workspace missing or smaller than pkv_decode_workspace_bytes";
+    case PKV_ERR_LAUNCH: return "kernel launch failed";
+    case PKV_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    case PKV_ERR_ALIAS: return "out overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+int64_t pkv_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_head,
+                               int32_t dtype_bytes) {
+  if (n_layers < 0 || n_kv_heads < 0 || d_head < 0 || dtype_bytes < 0) return -1;
+  return (int64_t)2 * n_layers * n_kv_heads * d_head * dtype_bytes;
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t d_head,
+                                  int32_t max_context_len, int32_t partition_tokens) {
+  const int32_t P = resolve_partition(partition_tokens);
+  if (num_seqs <= 0 || n_heads <= 0 || d_head <= 0 || max_context_len <= 0 || P <= 0 ||
+      P % pkv::kBlockTokens)
+    return 0;
+  const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
+  if (parts <= 1) return 0;
+  const size_t rows = (size_t)num_seqs * n_heads * (size_t)parts;
+  return 2 * align256(rows * sizeof(float)) + align256(rows * d_head * sizeof(float));
+}
+
+int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                      const int32_t* block_tables, const int32_t* positions,
+                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                      int32_t block_size, int32_t n_kv_heads, int32_t d_head, int32_t dtype,
+                      hipStream_t stream) {
+  if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !positions) return PKV_ERR_NULL;
+  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
+  if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
+  if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      n_kv_heads <= 0)
+    return PKV_ERR_SHAPE;
+  if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_ALIGN;
+  pkv::AppendArgs a;
+  a.k_pool = static_cast<char*>(k_pool);
+  a.v_pool = static_cast<char*>(v_pool);
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.block_tables = block_tables;
+  a.positions = positions;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.row_bytes = n_kv_heads * d_head * elem_bytes(dtype);
+  return pkv::launch_append(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int32_t pkv_gather_kv(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                      int32_t max_context_len, int32_t block_size, int32_t n_kv_heads,
+                      int32_t d_head, int32_t dtype, hipStream_t stream) {
+  if (!k_out || !v_out || !k_pool || !v_pool || !block_tables || !context_lens)
+    return PKV_ERR_NULL;
+  const int32_t st = check_pool_args(num_seqs, max_blocks_per_seq, num_blocks, max_context_len,
+                                     block_size, n_kv_heads, d_head, dtype);
+  if (st != PKV_OK) return st;
+  if (!aligned16(k_out) || !aligned16(v_out) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_ERR_ALIGN;
+  pkv::GatherArgs a;
+  a.k_out = static_cast<char*>(k_out);
+  a.v_out = static_cast<char*>(v_out);
+  a.k_pool = static_cast<const char*>(k_pool);
+  a.v_pool = static_cast<const char*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.row_bytes = n_kv_heads * d_head * elem_bytes(dtype);
+  return pkv::launch_gather(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* block_tables,
+                                   const int32_t* context_lens, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks,
+                                   int32_t max_context_len, int32_t block_size,
+                                   int32_t n_heads, int32_t n_kv_heads, int32_t d_head,
+                                   float scale, int32_t partition_tokens, int32_t dtype,
+                                   void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
+  int32_t st = check_pool_args(num_seqs, max_blocks_per_seq, num_blocks, max_context_len,
+                               block_size, n_kv_heads, d_head, dtype);
+  if (st != PKV_OK) return st;
+  if (!valid_group(n_heads, n_kv_heads)) return PKV_ERR_GROUP;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (partition_tokens < 0 || partition_tokens % pkv::kBlockTokens) return PKV_ERR_PARTITION;
+  const int32_t P = resolve_partition(partition_tokens);
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_ERR_ALIGN;
+  const size_t eb = (size_t)elem_bytes(dtype);
+  const size_t out_bytes = (size_t)num_seqs * n_heads * d_head * eb;
+  const size_t pool_bytes = (size_t)num_blocks * pkv::kBlockTokens * n_kv_heads * d_head * eb;
+  if (overlaps(out, out_bytes, q, out_bytes) || overlaps(out, out_bytes, k_pool, pool_bytes) ||
+      overlaps(out, out_bytes, v_pool, pool_bytes))
+    return PKV_ERR_ALIAS;
+
+  const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
+  const size_t need = pkv_decode_workspace_bytes(num_seqs, n_heads, d_head, max_context_len, P);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PKV_ERR_WORKSPACE;
+  if (parts > 65535) return PKV_ERR_PARTITION;   // grid x limit kept conservative
+
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_pool = static_cast<const char*>(k_pool);
+  a.v_pool = static_cast<const char*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.n_heads = n_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.partition_tokens = P;
+  a.max_partitions = (int32_t)parts;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+  if (need > 0) {
+    const size_t rows = (size_t)num_seqs * n_heads * (size_t)parts;
+    char* ws = static_cast<char*>(workspace);
+    a.ws_m = reinterpret_cast<float*>(ws);
+    a.ws_l = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
+    a.ws_o = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
+  } else {
+    a.ws_m = a.ws_l = a.ws_o = nullptr;
+  }
+  const hipError_t e = pkv::launch_decode(a, dtype, d_head, n_heads / n_kv_heads, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"

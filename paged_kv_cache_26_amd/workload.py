@@ -490,3 +490,30 @@ def relabel_blocks(wl: Workload, seed: int) -> Workload:
     refcount[perm] = wl.refcount
     return dataclasses.replace(wl, k_pool=k_pool, v_pool=v_pool, block_tables=tables,
                                refcount=refcount)
+
+
+def to_torch(wl: Workload, device="cuda"):
+    """The workload's arrays as torch tensors on ``device`` (bf16 reinterpreted from bits)."""
+    import torch
+
+    def conv(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(a).to(device)
+
+    return {
+        "k_pool": conv(wl.k_pool), "v_pool": conv(wl.v_pool),
+        "k_new": conv(wl.k_new), "v_new": conv(wl.v_new), "q": conv(wl.q),
+        "block_tables": torch.from_numpy(wl.block_tables).to(device),
+        "positions": torch.from_numpy(wl.positions).to(device),
+        "context_lens": torch.from_numpy(wl.context_lens).to(device),
+    }
+
+
+def from_torch(t, dtype: str) -> np.ndarray:
+    """A tensor back in the stored numpy representation (bf16 as uint16 bits)."""
+    import torch
+    t = t.detach().cpu().contiguous()
+    if dtype == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
