@@ -1,0 +1,257 @@
+"""Benchmark of one paged decode step (append + attention) on one MI355X.
+
+A step is one pass of the whole path over one batch: pkv_kv_append writes every
+sequence's new token into its slot, then pkv_paged_decode_attention (the split-KV decode
+kernel, plus the merge kernel when a sequence spans several partitions) attends over the
+paged context. Inputs are seeded synthetic workloads resident in HBM before timing; the
+same step is repeated (the new token is rewritten into the same slot, so every step does
+identical work).
+
+Prints ONE JSON line: the metric is KV GB/s read (whole step), with the decode launch's
+achieved bandwidth against the 8 TB/s HBM peak in "roofline", and the fp64 CPU oracle timed
+on a bounded sample of the same workload in "cpu_baseline".
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--partition 0] [--all]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
+
+# HBM bytes per decode launch (decode + merge kernels) from rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE runs, each scaled by what the counter reads for a 1 GiB device copy, keyed by
+# (workload id, partition_tokens). Each entry records the sha256 prefix of the decode kernel
+# source it was measured on; it is reported only while that source is unchanged.
+MEASURED_TRAFFIC = {
+    (2, 0): {"bytes": 1193217955, "decode_source_sha256": "0ef28e6feea7663d"},
+}
+DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", "pkv_decode.hip")
+
+
+def measured_traffic(cfg: int, partition: int):
+    import hashlib
+    entry = MEASURED_TRAFFIC.get((cfg, partition))
+    if entry is None:
+        return None
+    with open(DECODE_SOURCE, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()[:16]
+    return entry["bytes"] if sha == entry["decode_source_sha256"] else None
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="tokens per KV partition; 0 = the library's balanced split")
+    ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, copy a buffer of this many MiB 3 times (a dispatch of "
+                         "known traffic for scaling hardware byte counters)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time for the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes the method must move per step (see the design notes for the definition)."""
+    s = wl.spec
+    e = {"f32": 4, "f16": 2, "bf16": 2}[s.dtype]
+    kv = wl.kv_bytes_logical()
+    q_out = 2 * s.batch * s.n_heads * s.d_head * e
+    tables = int(sum(-(-int(n) // 16) for n in wl.context_lens)) * 4 + s.batch * 4
+    append = 2 * s.batch * s.n_kv_heads * s.d_head * e * 2 + s.batch * 4 * 2
+    return {"kv": kv, "kv_unique": wl.kv_bytes_unique(), "decode": kv + q_out + tables,
+            "append": append}
+
+
+def run_config(args, cfg: int, want_cpu: bool) -> dict:
+    import torch
+
+    from paged_kv_cache_26_amd import pkv
+    from paged_kv_cache_26_amd import workload as wlm
+
+    pkv.load_library()
+    t0 = time.time()
+    wl = wlm.make_workload(cfg)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda:0")
+    t = wlm.to_torch(wl, dev)
+    out = torch.empty_like(t["q"])
+    need = pkv.pkv_decode_workspace_bytes(wl.batch, wl.spec.n_heads, wl.spec.n_kv_heads,
+                                          wl.spec.d_head, wl.max_context_len, args.partition)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(mid_event):
+        pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"],
+                          t["block_tables"], t["positions"], stream=stream)
+        mid_event.record(stream)
+        pkv.pkv_paged_decode_attention(out, t["q"], t["k_pool"], t["v_pool"],
+                                       t["block_tables"], t["context_lens"],
+                                       wl.max_context_len, wl.scale, args.partition, ws, stream)
+
+    scratch_event = torch.cuda.Event(enable_timing=True)
+    for _ in range(args.warmup):
+        step(scratch_event)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(K):
+        ev_start[i].record(stream)
+        step(ev_mid[i])
+        ev_end[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = np.array([ev_start[i].elapsed_time(ev_end[i]) for i in range(K)])
+    dec_ms = np.array([ev_mid[i].elapsed_time(ev_end[i]) for i in range(K)])
+    total_ms = ev_start[0].elapsed_time(ev_end[K - 1])
+    ms_per_step = total_ms / K
+    by = algorithmic_bytes(wl)
+    value = by["kv"] / (ms_per_step * 1e-3) / 1e9
+    dec_avg_s = float(dec_ms.mean()) * 1e-3
+    achieved = by["decode"] / dec_avg_s / 1e9
+
+    spec = wl.spec
+    res = {
+        "metric": "paged decode attention: KV GB/s read and % of MI355X HBM peak; us/step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded)",
+        "config": {
+            "workload": spec.name,
+            "batch": spec.batch, "n_heads": spec.n_heads, "n_kv_heads": spec.n_kv_heads,
+            "d_head": spec.d_head, "block_size": 16,
+            "context_tokens": int(wl.context_lens.sum()),
+            "max_context_len": wl.max_context_len,
+            "kv_split": ("balanced split over the GPU" if args.partition == 0
+                         else f"fixed {args.partition}-token partitions"),
+            "kv_bytes_per_step": by["kv"], "kv_unique_bytes_per_step": by["kv_unique"],
+            "parallelism": "single GPU",
+        },
+        "timing": {
+            "step_us_median": round(float(np.median(step_ms)) * 1e3, 2),
+            "step_us_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
+            "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+            "decode_us_mean": round(dec_avg_s * 1e6, 2),
+            "decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
+            "decode_kv_gbps": round(by["kv"] / dec_avg_s / 1e9, 2),
+            "host_wall_us_per_step": round(wall / K * 1e6, 2),
+            "workload_gen_s": round(gen_s, 1),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged decode launch (decode kernel + partition merge)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(cfg, args.partition),
+            "algorithmic_bytes_per_launch": by["decode"],
+        },
+    }
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = {"read": n, "write": n}
+        del src, dst
+    if cfg == 5:
+        res["timing"]["decode_unique_gbps"] = round(by["kv_unique"] / dec_avg_s / 1e9, 2)
+    if want_cpu:
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    # free device memory before the next workload
+    del t, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, target_s: float) -> dict:
+    """The fp64 oracle, unchanged, on a bounded sample: whole sequences in order until the
+    time budget is spent; GB/s = KV bytes of those sequences / oracle time."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pkv_oracle as orc
+
+    kp, vp = orc.kv_append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.block_tables,
+                           wl.positions, 16)
+    s = wl.spec
+    e = {"f32": 4, "f16": 2, "bf16": 2}[s.dtype]
+    done_bytes, done_seqs, spent = 0, 0, 0.0
+    with threadpool_limits(limits=1):
+        while spent < target_s:
+            for b in range(wl.batch):
+                pairs = [(b, h) for h in range(s.n_heads)]
+                t0 = time.perf_counter()
+                orc.paged_decode_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                           wl.scale, wl.dtype, pairs=pairs)
+                spent += time.perf_counter() - t0
+                done_bytes += int(wl.context_lens[b]) * 2 * s.n_kv_heads * s.d_head * e
+                done_seqs += 1
+                if spent >= target_s:
+                    break
+    return {
+        "value": round(done_bytes / spent / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{done_seqs} sequence passes (all heads) over the {wl.batch}-sequence "
+                  f"batch in order; {done_bytes} KV bytes in {spent:.1f} s",
+        "cpu": platform.processor() or platform.machine(),
+        "host_cpus_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    if os.environ.get("WORLD_SIZE", "1") != "1":
+        print("this build runs on one GPU only", file=sys.stderr)
+        sys.exit(2)
+    cfgs = [1, 2, 3, 4, 5] if args.all else [args.config]
+    for cfg in cfgs:
+        res = run_config(args, cfg, want_cpu=not args.no_cpu_baseline)
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -115,9 +115,16 @@ int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void*
  *                   ceil(N_b / 16) entries, gets NaN outputs.
  *   max_context_len host-side upper bound of context_lens; sizes the launch grid.
  *   scale           score multiplier, normally 1/sqrt(d_head).
- *   partition_tokens tokens per KV partition (a multiple of 16); 0 selects 512. A
- *                   sequence longer than one partition is processed by several
- *                   workgroups whose partial results a second kernel merges.
+ *   partition_tokens 0 (default): balanced split. The list of (KV-head group, sequence,
+ *                   16-token block) units is cut into equal contiguous shares, one per
+ *                   resident workgroup of the GPU, so every compute unit streams the same
+ *                   number of KV bytes whatever the mix of context lengths; a sequence cut
+ *                   between workgroups is finished by a merge kernel. Used when
+ *                   max_context_len > 512 and num_seqs <= 4096; otherwise 0 selects fixed
+ *                   512-token partitions (a single kernel when max_context_len <= 512).
+ *                   > 0: fixed partitions of that many tokens (a multiple of 16); a sequence
+ *                   longer than one partition is processed by several workgroups whose
+ *                   partial results the merge kernel combines.
  *   workspace       device scratch of at least pkv_decode_workspace_bytes(...) bytes
  *                   (may be NULL when that size is 0); its contents on entry do not
  *                   matter and on return are unspecified.
@@ -136,16 +143,21 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
                                    hipStream_t stream);
 
 /*
- * pkv_decode_workspace_bytes - scratch bytes pkv_paged_decode_attention needs (host
- * only, no device call). 0 when every sequence fits one partition. Returns 0 for
- * invalid sizes as well; pkv_paged_decode_attention then reports the invalid argument.
+ * pkv_decode_workspace_bytes - scratch bytes pkv_paged_decode_attention needs for these
+ * sizes (host only, no device call). 0 when no partial results are needed (fixed
+ * partitions with every sequence in one partition). Returns 0 for invalid sizes as well;
+ * pkv_paged_decode_attention then reports the invalid argument.
  *
- * Layout (fp32, 256-byte aligned sections): running maxima [num_seqs, n_heads, P],
- * sums [num_seqs, n_heads, P], unnormalised outputs [num_seqs, n_heads, P, d_head], with
- * P = ceil(max_context_len / partition_tokens).
+ * Contents: fp32 partial-result records (running maximum, running sum, unnormalised
+ * output of d_head values) and, in the balanced split, num_seqs + 1 int32 block prefix
+ * sums. Fixed partitions hold num_seqs * n_heads * ceil(max_context_len /
+ * partition_tokens) records; the balanced split at most (1024 + ceil(n_kv_heads / NW) *
+ * num_seqs) * NW * (n_heads / n_kv_heads) records, NW = 8 if n_kv_heads is a multiple of
+ * 8, else 4.
  */
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t d_head,
-                                  int32_t max_context_len, int32_t partition_tokens);
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads,
+                                  int32_t d_head, int32_t max_context_len,
+                                  int32_t partition_tokens);
 
 /*
  * pkv_kv_bytes_per_token - bytes one token occupies in the KV cache of a whole model:

@@ -26,11 +26,41 @@ bool valid_group(int32_t n_heads, int32_t n_kv_heads) {
   return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
-int32_t resolve_partition(int32_t partition_tokens) {
-  return partition_tokens == 0 ? pkv::kDefaultPartition : partition_tokens;
-}
-
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// How a decode call splits its work, and the workspace that needs.
+struct Plan {
+  bool split;            // balanced split over the GPU
+  int32_t partition;     // fixed mode: tokens per partition
+  int64_t parts;         // fixed mode: partitions of the longest sequence
+  size_t records;        // partial-result records the workspace must hold
+  size_t prefix_ints;    // split mode: block prefix sums
+  size_t bytes;          // total workspace bytes
+};
+
+Plan make_plan(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads, int32_t d_head,
+               int32_t max_context_len, int32_t partition_tokens) {
+  Plan p{};
+  // 0 selects the balanced split, except when every sequence fits one 512-token partition
+  // (one kernel, no merge) or there are more sequences than the split mode holds.
+  p.split = partition_tokens == 0 && num_seqs <= pkv::kSplitMaxSeqs &&
+            max_context_len > pkv::kFallbackPartition;
+  if (p.split) {
+    const int64_t nw = pkv::max_waves_per_workgroup(n_kv_heads);
+    const int64_t hg = (n_kv_heads + nw - 1) / nw;
+    const int64_t g = n_heads / n_kv_heads;
+    p.records = (size_t)((pkv::kSplitMaxWorkgroups + hg * num_seqs) * nw * g);
+    p.prefix_ints = (size_t)num_seqs + 1;
+  } else {
+    p.partition = partition_tokens == 0 ? pkv::kFallbackPartition : partition_tokens;
+    p.parts = ((int64_t)max_context_len + p.partition - 1) / p.partition;
+    p.records = p.parts > 1 ? (size_t)num_seqs * n_heads * (size_t)p.parts : 0;
+  }
+  if (p.records > 0)
+    p.bytes = align256(p.prefix_ints * sizeof(int32_t)) + 2 * align256(p.records * sizeof(float)) +
+              align256(p.records * d_head * sizeof(float));
+  return p;
+}
 
 // Byte ranges [a, a + na) and [b, b + nb) overlap.
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -82,16 +112,14 @@ int64_t pkv_kv_bytes_per_token(int32_t n_layers, int32_t n_kv_heads, int32_t d_h
   return (int64_t)2 * n_layers * n_kv_heads * d_head * dtype_bytes;
 }
 
-size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t d_head,
-                                  int32_t max_context_len, int32_t partition_tokens) {
-  const int32_t P = resolve_partition(partition_tokens);
-  if (num_seqs <= 0 || n_heads <= 0 || d_head <= 0 || max_context_len <= 0 || P <= 0 ||
-      P % pkv::kBlockTokens)
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads,
+                                  int32_t d_head, int32_t max_context_len,
+                                  int32_t partition_tokens) {
+  if (num_seqs <= 0 || n_heads <= 0 || d_head <= 0 || max_context_len <= 0 ||
+      !valid_group(n_heads, n_kv_heads) || partition_tokens < 0 ||
+      partition_tokens % pkv::kBlockTokens)
     return 0;
-  const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
-  if (parts <= 1) return 0;
-  const size_t rows = (size_t)num_seqs * n_heads * (size_t)parts;
-  return 2 * align256(rows * sizeof(float)) + align256(rows * d_head * sizeof(float));
+  return make_plan(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, partition_tokens).bytes;
 }
 
 int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
@@ -165,7 +193,6 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
   if (!valid_group(n_heads, n_kv_heads)) return PKV_ERR_GROUP;
   if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
   if (partition_tokens < 0 || partition_tokens % pkv::kBlockTokens) return PKV_ERR_PARTITION;
-  const int32_t P = resolve_partition(partition_tokens);
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKV_ERR_ALIGN;
   const size_t eb = (size_t)elem_bytes(dtype);
@@ -175,13 +202,13 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
       overlaps(out, out_bytes, v_pool, pool_bytes))
     return PKV_ERR_ALIAS;
 
-  const int64_t parts = ((int64_t)max_context_len + P - 1) / P;
-  const size_t need = pkv_decode_workspace_bytes(num_seqs, n_heads, d_head, max_context_len, P);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+  const Plan plan = make_plan(num_seqs, n_heads, n_kv_heads, d_head, max_context_len,
+                              partition_tokens);
+  if (!plan.split && plan.parts > 65535) return PKV_ERR_PARTITION;   // grid y limit
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned16(workspace)))
     return PKV_ERR_WORKSPACE;
-  if (parts > 65535) return PKV_ERR_PARTITION;   // grid x limit kept conservative
 
-  pkv::DecodeArgs a;
+  pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;
   a.k_pool = static_cast<const char*>(k_pool);
@@ -194,17 +221,18 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
   a.max_context_len = max_context_len;
   a.n_heads = n_heads;
   a.n_kv_heads = n_kv_heads;
-  a.partition_tokens = P;
-  a.max_partitions = (int32_t)parts;
+  a.split = plan.split ? 1 : 0;
+  a.partition_tokens = plan.partition;
+  a.max_partitions = (int32_t)plan.parts;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
-  if (need > 0) {
-    const size_t rows = (size_t)num_seqs * n_heads * (size_t)parts;
+  if (plan.bytes > 0) {
     char* ws = static_cast<char*>(workspace);
-    a.ws_m = reinterpret_cast<float*>(ws);
-    a.ws_l = reinterpret_cast<float*>(ws + align256(rows * sizeof(float)));
-    a.ws_o = reinterpret_cast<float*>(ws + 2 * align256(rows * sizeof(float)));
-  } else {
-    a.ws_m = a.ws_l = a.ws_o = nullptr;
+    const size_t pre = align256(plan.prefix_ints * sizeof(int32_t));
+    const size_t vec = align256(plan.records * sizeof(float));
+    a.ws_prefix = plan.prefix_ints ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    a.ws_m = reinterpret_cast<float*>(ws + pre);
+    a.ws_l = reinterpret_cast<float*>(ws + pre + vec);
+    a.ws_o = reinterpret_cast<float*>(ws + pre + 2 * vec);
   }
   const hipError_t e = pkv::launch_decode(a, dtype, d_head, n_heads / n_kv_heads, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;

@@ -10,13 +10,14 @@
 // (scale * log2 e folded into one multiplier), which leaves the result unchanged.
 //
 // Work decomposition (FlashDecoding, "Scaling Book 第 11 章" §11.8): a sequence's tokens
-// are cut into partitions of P tokens (a multiple of the 16-token block). One workgroup
-// of 4 waves handles one (partition, KV head, sequence) and all G query heads of that KV
-// head, so each K/V byte is read from HBM once per KV head. Waves take the partition's
-// blocks round-robin; each keeps its own (m, l, O) and the four are merged through LDS.
-// A sequence with one partition is finished in place; otherwise the workgroup writes its
-// (m, l, O) to the workspace and merge_kernel combines the partitions by the same
-// rescale rule.
+// are cut into partitions of P tokens (a multiple of the 16-token block). One wave owns
+// one (KV head, partition, sequence) and all G query heads of that KV head, so each K/V
+// byte is read from HBM once. A workgroup holds NW waves = NW consecutive KV heads of the
+// same partition: together they read whole token rows (all heads of a token are
+// contiguous in the pool), which keeps each compute unit's request stream on neighbouring
+// bytes. Waves never wait for each other. A sequence with one partition is finished in
+// place; otherwise each wave writes its (m, l, O) to the workspace and merge_kernel
+// combines the partitions by the same rescale rule.
 //
 // Per 16-token block, inside one wave (lane = 16 * r + c, r = 0..3, c = 0..15):
 //   * QK^T on the matrix cores. The K tile is the MFMA A operand (row = token c of the
@@ -31,7 +32,9 @@
 //   * P.V on the vector ALU in fp32: lane (r, c) loads d_head/16 consecutive elements
 //     (chunk c) of token 4r + jj for jj = 0..3, and gets each head's probability for that
 //     token from lane (r, h) with a DPP row broadcast.
-// K and V of block i+1 are loaded while block i is computed (two register buffers).
+// K and V are prefetched kDepth blocks ahead into registers. V rows are read with the
+// non-temporal hint (each byte is used once); K keeps the default policy because two
+// consecutive loads of a wave share each 128-byte line.
 
 #include "pkv_internal.h"
 
@@ -43,6 +46,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 
 template <int DT> struct ElemBytes { static constexpr int value = DT == 0 ? 4 : 2; };
 
@@ -105,6 +110,9 @@ struct Geo {
   static constexpr int kNK = kRow / 64;        // 16-byte K loads per lane per block
   static constexpr int kEPL = D / 16;          // V elements per lane per token
   static constexpr int kVW = kEPL * kE / 4;    // V 32-bit words per lane per token
+  // Blocks loaded ahead of the one being computed: two, unless one block already takes
+  // 64 registers per lane (fp32 with d_head 128).
+  static constexpr int kDepth = (4 * kNK + 4 * kVW) <= 32 ? 2 : 1;
 };
 
 // One block's K and V as held by one lane.
@@ -126,17 +134,16 @@ __device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kblk, cons
   for (int jj = 0; jj < 4; ++jj) {
     const char* src = vp + jj * tok_stride;
     if constexpr (G_::kVW == 8) {
-      const u32x4 a0 = reinterpret_cast<const u32x4*>(src)[0];
-      const u32x4 a1 = reinterpret_cast<const u32x4*>(src)[1];
+      const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      const u32x4 a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + 1);
 #pragma unroll
       for (int x = 0; x < 4; ++x) { t.v[jj][x] = a0[x]; t.v[jj][4 + x] = a1[x]; }
     } else if constexpr (G_::kVW == 4) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(src);
+      const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
 #pragma unroll
       for (int x = 0; x < 4; ++x) t.v[jj][x] = a0[x];
     } else {
-      typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 a0 = *reinterpret_cast<const u32x2*>(src);
+      const u32x2 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
       t.v[jj][0] = a0[0];
       t.v[jj][1] = a0[1];
     }
@@ -150,10 +157,11 @@ struct WaveState {
   float o[G][Geo<DT, D>::kEPL] = {};   // lane-partial O[h][chunk c] for its row's tokens
 };
 
+// One 16-token block starting at token blk_tok0; tokens >= tok_end are masked.
 template <int DT, int D, int G>
 __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Tile<DT, D>& t,
-                                              const u32x4 (&qf)[Geo<DT, D>::kNK], int tok0,
-                                              int tok_end, float scale_log2) {
+                                              const u32x4 (&qf)[Geo<DT, D>::kNK], int blk_tok0,
+                                              int tok_end, float scale_log2, int r) {
   using G_ = Geo<DT, D>;
   // S^T[token][head] for this block on the matrix cores.
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -171,9 +179,17 @@ __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Til
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(t.k[kk][s]), as_f(qf[kk][s]), acc, 0, 0, 0);
     }
   }
+  // Only the last block of a sequence can be partial (partitions are block aligned).
+  const bool partial = blk_tok0 + kBlockTokens > tok_end;
+  const int tok0 = blk_tok0 + 4 * r;
   float s[4];
+  if (partial) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s[i] = (tok0 + i < tok_end) ? acc[i] * scale_log2 : -INFINITY;
+    for (int i = 0; i < 4; ++i) s[i] = (tok0 + i < tok_end) ? acc[i] * scale_log2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = acc[i] * scale_log2;
+  }
 
   float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   bm = fmaxf(bm, __shfl_xor(bm, 16));
@@ -197,9 +213,11 @@ __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Til
   for (int jj = 0; jj < 4; ++jj) {
     float v[G_::kEPL];
     widen<DT, G_::kVW>(t.v[jj], v);
-    const bool valid = tok0 + jj < tok_end;
+    if (partial) {
+      const bool valid = tok0 + jj < tok_end;
 #pragma unroll
-    for (int e = 0; e < G_::kEPL; ++e) v[e] = valid ? v[e] : 0.f;   // unused slots may hold NaN
+      for (int e = 0; e < G_::kEPL; ++e) v[e] = valid ? v[e] : 0.f;   // unused slots may hold NaN
+    }
     static_for<G>([&](auto hc) {
       constexpr int h = decltype(hc)::value;
       const float ph = row_bcast<h>(p[jj]);
@@ -209,38 +227,53 @@ __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Til
   }
 }
 
-template <int DT, int D, int G>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
-  using G_ = Geo<DT, D>;
-  constexpr int W = kDecodeWaves;
-  const int p = blockIdx.x, j = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r = lane >> 4, c = lane & 15;
-  const int H = a.n_heads;
-
-  __shared__ float sm_m[W][G], sm_l[W][G];
-  __shared__ float sm_o[W][G][D];
-  __shared__ int sm_bad[W];
-
-  const int n_ctx = a.context_lens[b];
-  if (n_ctx < 1 || n_ctx > a.max_context_len) {
-    if (p == 0)
-      for (int i = tid; i < G * D; i += 256)
-        store_elem<DT>(a.out, ((size_t)b * H + j * G) * D + i, __builtin_nanf(""));
-    return;
+// Store EPL consecutive outputs of one lane (16 or 8 bytes for 16-bit types).
+template <int DT, int EPL>
+__device__ __forceinline__ void store_row_chunk(void* base, size_t idx, const float* v) {
+  if constexpr (DT == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const f32x4 x = {v[e], v[e + 1], v[e + 2], v[e + 3]};
+      *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx + e) = x;
+    }
+  } else {
+    unsigned w[EPL / 2];
+#pragma unroll
+    for (int e = 0; e < EPL; e += 2) {
+      if constexpr (DT == 1) {
+        const f16x2 h = {(_Float16)v[e], (_Float16)v[e + 1]};
+        w[e / 2] = __builtin_bit_cast(unsigned, h);
+      } else {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 h = {(__bf16)v[e], (__bf16)v[e + 1]};
+        w[e / 2] = __builtin_bit_cast(unsigned, h);
+      }
+    }
+    if constexpr (EPL == 8) {
+      const u32x4 x = {w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<u32x4*>(static_cast<char*>(base) + idx * 2) = x;
+    } else {
+      const u32x2 x = {w[0], w[1]};
+      *reinterpret_cast<u32x2*>(static_cast<char*>(base) + idx * 2) = x;
+    }
   }
-  const int P = a.partition_tokens;
-  const int n_part = (n_ctx + P - 1) / P;
-  if (p >= n_part) return;
-  const int tok_end = min(n_ctx, (p + 1) * P);
-  const int blk_begin = (p * P) >> 4;
-  const int blk_end = (tok_end + 15) >> 4;
-  const int n_my = (blk_end - blk_begin - wave + W - 1) / W;   // this wave's blocks (may be 0)
+}
+
+// One wave: blocks [blk_begin, blk_begin + n_my) of sequence b, KV head j, into st
+// (lane-partial; finish_rows completes it). Tokens >= tok_end are masked. bad is set if a
+// table entry is outside the pool (the data of that block is then not read).
+template <int DT, int D, int G>
+__device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const DecodeArgs& a,
+                                       int b, int j, int blk_begin, int n_my, int tok_end,
+                                       int lane) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  const size_t head_row0 = (size_t)b * a.n_heads + (size_t)j * G;
 
   // Query fragments (MFMA B operand): head c of this KV group, zero for c >= G.
   u32x4 qf[G_::kNK];
   {
-    const char* qrow = static_cast<const char*>(a.q) + ((size_t)b * H + j * G + (c < G ? c : 0)) * G_::kRow;
+    const char* qrow = static_cast<const char*>(a.q) + (head_row0 + (c < G ? c : 0)) * G_::kRow;
 #pragma unroll
     for (int kk = 0; kk < G_::kNK; ++kk) {
       const u32x4 z = {0u, 0u, 0u, 0u};
@@ -253,14 +286,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const size_t head_off = (size_t)j * G_::kRow;
   const size_t k_lane = head_off + c * tok_stride + 16 * r;
   const size_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
-  const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq;
+  const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_begin;
 
-  WaveState<DT, D, G> st;
-  int bad = 0;
-  int tbl = 0;   // lane i holds the table entry of this wave's block (chunk * 64 + i)
+  int tbl = 0;   // lane i holds the table entry of block (chunk * 64 + i) of the range
   auto load_table = [&](int first) {
     const int i = first + lane;
-    tbl = i < n_my ? trow[blk_begin + wave + i * W] : 0;
+    tbl = i < n_my ? trow[i] : 0;
   };
   auto fetch = [&](Tile<DT, D>& t, int i) {
     int pb = __builtin_amdgcn_readlane(tbl, i & 63);
@@ -270,102 +301,260 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     load_tile<DT, D>(t, a.k_pool + (size_t)pb * blk_stride, a.v_pool + (size_t)pb * blk_stride,
                      k_lane, v_lane, tok_stride);
   };
-  auto tok0_of = [&](int i) { return (blk_begin + wave + i * W) * kBlockTokens + 4 * r; };
 
-  if (n_my > 0) {
-    Tile<DT, D> ta, tb;
-    load_table(0);
-    fetch(ta, 0);
-    for (int i = 0; i < n_my; i += 2) {
-      if (i + 1 < n_my) {
-        if (((i + 1) & 63) == 0) load_table(i + 1);
-        fetch(tb, i + 1);
+  constexpr int kDepth = G_::kDepth;
+  constexpr int NB = kDepth + 1;
+  Tile<DT, D> tt[NB];
+  load_table(0);
+#pragma unroll
+  for (int d0 = 0; d0 < kDepth; ++d0)
+    if (d0 < n_my) fetch(tt[d0], d0);
+  for (int i0 = 0; i0 < n_my; i0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      if (i >= n_my) break;
+      if (i + kDepth < n_my) {
+        if (((i + kDepth) & 63) == 0) load_table(i + kDepth);
+        fetch(tt[(u + kDepth) % NB], i + kDepth);
       }
-      process_block<DT, D, G>(st, ta, qf, tok0_of(i), tok_end, a.scale_log2);
-      if (i + 1 >= n_my) break;
-      if (i + 2 < n_my) {
-        if (((i + 2) & 63) == 0) load_table(i + 2);
-        fetch(ta, i + 2);
-      }
-      process_block<DT, D, G>(st, tb, qf, tok0_of(i + 1), tok_end, a.scale_log2);
+      process_block<DT, D, G>(st, tt[u], qf, (blk_begin + i) * kBlockTokens, tok_end,
+                              a.scale_log2, r);
     }
   }
+}
 
-  // Reduce the lane-partial l and O over the four rows, then merge the waves via LDS.
+// Sum the lane-partial l and O over the four rows: afterwards every lane holds l of
+// head c, and lane (r, c) holds O[h][chunk c] for every head h.
+template <int DT, int D, int G>
+__device__ __forceinline__ void finish_rows(WaveState<DT, D, G>& st) {
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < G_::kEPL; ++e) {
+    for (int e = 0; e < Geo<DT, D>::kEPL; ++e) {
       st.o[h][e] += __shfl_xor(st.o[h][e], 16);
       st.o[h][e] += __shfl_xor(st.o[h][e], 32);
     }
-  if (r == 0) {
-    if (c < G) {
-      sm_m[wave][c] = st.m;
-      sm_l[wave][c] = st.l;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < G_::kEPL; ++e) sm_o[wave][h][c * G_::kEPL + e] = st.o[h][e];
-  }
-  if (lane == 0) sm_bad[wave] = bad;
-  __syncthreads();
+}
 
-  int any_bad = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) any_bad |= sm_bad[w];
+// out[head_row0 + h] = O[h] / l[h] for the G heads of the wave.
+template <int DT, int D, int G>
+__device__ __forceinline__ void write_final(const DecodeArgs& a, const WaveState<DT, D, G>& st,
+                                            int bad, size_t head_row0, int lane) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  float inv[G];
+  static_for<G>([&](auto hc) {
+    constexpr int h = decltype(hc)::value;
+    inv[h] = 1.0f / row_bcast<h>(st.l);
+  });
+  if (r != 0) return;
   const float qnan = __builtin_nanf("");
-  for (int i = tid; i < G * D; i += 256) {
-    const int h = i / D, dd = i - h * D;
-    float M = sm_m[0][h];
 #pragma unroll
-    for (int w = 1; w < W; ++w) M = fmaxf(M, sm_m[w][h]);
-    float L = 0.f, O = 0.f;
+  for (int h = 0; h < G; ++h) {
+    float v[G_::kEPL];
 #pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float f = exp2_fast(sm_m[w][h] - M);   // 0 for a wave that saw no block
-      L = fmaf(sm_l[w][h], f, L);
-      O = fmaf(sm_o[w][h][dd], f, O);
-    }
-    const size_t row = (size_t)b * H + j * G + h;
-    if (n_part == 1) {
-      store_elem<DT>(a.out, row * D + dd, any_bad ? qnan : O / L);
-    } else {
-      const size_t slot = row * a.max_partitions + p;
-      a.ws_o[slot * D + dd] = any_bad ? qnan : O;
-      if (dd == 0) {
-        a.ws_m[slot] = any_bad ? qnan : M;
-        a.ws_l[slot] = any_bad ? qnan : L;
-      }
-    }
+    for (int e = 0; e < G_::kEPL; ++e) v[e] = bad ? qnan : st.o[h][e] * inv[h];
+    store_row_chunk<DT, G_::kEPL>(a.out, (head_row0 + h) * D + c * G_::kEPL, v);
   }
 }
 
-// One workgroup per (sequence, query head): combine that head's partitions.
+// Partial record of head h at index rec0 + h * rec_stride.
+template <int DT, int D, int G>
+__device__ __forceinline__ void write_record(const DecodeArgs& a, const WaveState<DT, D, G>& st,
+                                             int bad, size_t rec0, size_t rec_stride, int lane) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  if (r != 0) return;
+  const float qnan = __builtin_nanf("");
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float* dst = a.ws_o + (rec0 + h * rec_stride) * D + c * G_::kEPL;
+#pragma unroll
+    for (int e = 0; e < G_::kEPL; e += 4) {
+      const f32x4 x = {bad ? qnan : st.o[h][e], bad ? qnan : st.o[h][e + 1],
+                       bad ? qnan : st.o[h][e + 2], bad ? qnan : st.o[h][e + 3]};
+      *reinterpret_cast<f32x4*>(dst + e) = x;
+    }
+  }
+  if (c < G) {
+    const size_t rec = rec0 + c * rec_stride;
+    a.ws_m[rec] = bad ? qnan : st.m;
+    a.ws_l[rec] = bad ? qnan : st.l;
+  }
+}
+
 template <int DT, int D>
+__device__ __forceinline__ void write_nan_rows(const DecodeArgs& a, size_t row0, int rows,
+                                               int tid, int nthreads) {
+  for (int i = tid; i < rows * D; i += nthreads)
+    store_elem<DT>(a.out, row0 * D + i, __builtin_nanf(""));
+}
+
+// Fixed partitions: workgroup = NW waves = KV heads hg*NW .. hg*NW+NW-1 of one
+// (partition, sequence); grid (head groups, partitions, sequences).
+template <int DT, int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
+  const int hg = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int j = hg * NW + wave;                 // this wave's KV head
+  if (j >= a.n_kv_heads) return;                // no barrier below: waves are independent
+  const size_t head_row0 = (size_t)b * a.n_heads + (size_t)j * G;
+
+  const int n_ctx = a.context_lens[b];
+  if (n_ctx < 1 || n_ctx > a.max_context_len) {
+    if (p == 0) write_nan_rows<DT, D>(a, head_row0, G, lane, 64);
+    return;
+  }
+  const int P = a.partition_tokens;
+  const int n_part = (n_ctx + P - 1) / P;
+  if (p >= n_part) return;
+  const int tok_end = min(n_ctx, (p + 1) * P);
+  const int blk_begin = (p * P) >> 4;
+  const int n_my = ((tok_end + 15) >> 4) - blk_begin;     // >= 1
+
+  WaveState<DT, D, G> st;
+  int bad = 0;
+  attend<DT, D, G>(st, bad, a, b, j, blk_begin, n_my, tok_end, lane);
+  finish_rows<DT, D, G>(st);
+  if (n_part == 1)
+    write_final<DT, D, G>(a, st, bad, head_row0, lane);
+  else
+    write_record<DT, D, G>(a, st, bad, head_row0 * a.max_partitions + p, a.max_partitions, lane);
+}
+
+// Balanced split: the work is the list of units (head group hg, sequence b, block k) in
+// that order, T units in all. Workgroup w of the W in the grid takes units
+// [w*T/W, (w+1)*T/W) — every workgroup gets the same number of blocks to stream, whatever
+// the mix of context lengths. The part of one sequence inside one workgroup is a
+// segment; a segment holding a whole sequence is finished in place, any other one leaves
+// a record for merge_kernel. Segments of stream s = hg * num_seqs + b are produced by
+// consecutive workgroups in increasing order of w, so (w + s) names each segment
+// uniquely: its G records start at ((w + s) * NW + wave) * G.
+template <int DT, int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
+  constexpr int kThreads = 64 * NW;
+  __shared__ int sm_pref[kSplitMaxSeqs + 1];   // blocks of sequences before b
+  __shared__ int sm_scan[kThreads];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = a.num_seqs;
+
+  // Exclusive prefix sum of the block counts (sequences with an invalid length count 0).
+  const int chunk = (B + kThreads - 1) / kThreads;
+  const int s0 = min(B, tid * chunk), s1 = min(B, s0 + chunk);
+  int run = 0;
+  for (int s = s0; s < s1; ++s) {
+    const int n = a.context_lens[s];
+    sm_pref[s] = run;
+    run += (n >= 1 && n <= a.max_context_len) ? (n + kBlockTokens - 1) / kBlockTokens : 0;
+  }
+  sm_scan[tid] = run;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int v = tid >= off ? sm_scan[tid - off] : 0;
+    __syncthreads();
+    sm_scan[tid] += v;
+    __syncthreads();
+  }
+  const int before = tid > 0 ? sm_scan[tid - 1] : 0;
+  for (int s = s0; s < s1; ++s) sm_pref[s] += before;
+  if (tid == kThreads - 1) sm_pref[B] = sm_scan[kThreads - 1];
+  __syncthreads();
+
+  const int w = blockIdx.x;
+  const int HG = (a.n_kv_heads + NW - 1) / NW;
+  const int T1 = sm_pref[B];                    // blocks per head group
+  const long long T = (long long)T1 * HG;
+  // Workgroups in use: at most W, and at least kSplitMinBlocks blocks each.
+  const long long W = min((long long)gridDim.x, (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
+  if (w == 0)
+    for (int s = tid; s <= B; s += kThreads) a.ws_prefix[s] = sm_pref[s];
+  for (int s = w; s < B; s += gridDim.x) {      // invalid lengths: NaN outputs
+    const int n = a.context_lens[s];
+    if (n < 1 || n > a.max_context_len)
+      write_nan_rows<DT, D>(a, (size_t)s * a.n_heads, a.n_heads, tid, kThreads);
+  }
+  if (w >= W) return;
+  const long long u1 = (w + 1) * T / W;
+  long long u = w * T / W;
+  while (u < u1) {
+    const int hg = (int)(u / T1);
+    const int rem = (int)(u - (long long)hg * T1);
+    int lo = 0, hi = B;                         // last b with sm_pref[b] <= rem
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sm_pref[mid] <= rem) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int blk0 = rem - sm_pref[b];
+    const int nb = sm_pref[b + 1] - sm_pref[b];
+    const long long seg_end = min(u1, (long long)hg * T1 + sm_pref[b + 1]);
+    const int n_my = (int)(seg_end - u);
+    const int j = hg * NW + wave;
+    if (j < a.n_kv_heads) {
+      const int tok_end = min(a.context_lens[b], (blk0 + n_my) * kBlockTokens);
+      WaveState<DT, D, G> st;
+      int bad = 0;
+      attend<DT, D, G>(st, bad, a, b, j, blk0, n_my, tok_end, lane);
+      finish_rows<DT, D, G>(st);
+      const size_t head_row0 = (size_t)b * a.n_heads + (size_t)j * G;
+      if (blk0 == 0 && n_my == nb) {
+        write_final<DT, D, G>(a, st, bad, head_row0, lane);
+      } else {
+        const long long stream = (long long)hg * B + b;
+        write_record<DT, D, G>(a, st, bad, ((size_t)(w + stream) * NW + wave) * G, 1, lane);
+      }
+    }
+    u = seg_end;
+  }
+}
+
+// One workgroup per (sequence, query head): combine that head's records by the rescale
+// rule. Fixed mode: the head's partitions. Split mode: the segments of its stream.
+template <int DT, int D, int NW>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int Q4 = D / 4;          // float4 chunks per output row
-  constexpr int PR = 256 / Q4;       // partitions read side by side
+  constexpr int PR = 256 / Q4;       // records read side by side
   const int bh = blockIdx.x;
-  const int b = bh / a.n_heads;
+  const int b = bh / a.n_heads, h = bh - b * a.n_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_ctx = a.context_lens[b];
   if (n_ctx < 1 || n_ctx > a.max_context_len) return;     // decode wrote NaN
-  const int n_part = (n_ctx + a.partition_tokens - 1) / a.partition_tokens;
-  if (n_part <= 1) return;                               // decode wrote the output
 
-  const float* m = a.ws_m + (size_t)bh * a.max_partitions;
-  const float* l = a.ws_l + (size_t)bh * a.max_partitions;
-  const float* o = a.ws_o + (size_t)bh * a.max_partitions * D;
+  size_t base, stride;
+  int n_rec;
+  if (a.split) {
+    const int B = a.num_seqs;
+    const int G = a.n_heads / a.n_kv_heads;
+    const int j = h / G, hh = h - j * G;
+    const int hg = j / NW, wv = j - hg * NW;
+    const int HG = (a.n_kv_heads + NW - 1) / NW;
+    const int T1 = a.ws_prefix[B];
+    const long long T = (long long)T1 * HG;
+    const long long W = min((long long)a.split_workgroups, (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
+    const int nb = a.ws_prefix[b + 1] - a.ws_prefix[b];
+    const long long U = (long long)hg * T1 + a.ws_prefix[b];
+    // workgroup owning unit x: the largest w with w*T/W <= x
+    const long long first = ((U + 1) * W - 1) / T;
+    const long long last = ((U + nb) * W - 1) / T;
+    if (first == last) return;                              // decode wrote the output
+    n_rec = (int)(last - first + 1);
+    base = ((size_t)(first + (long long)hg * B + b) * NW + wv) * G + hh;
+    stride = (size_t)NW * G;
+  } else {
+    n_rec = (n_ctx + a.partition_tokens - 1) / a.partition_tokens;
+    if (n_rec <= 1) return;                                 // decode wrote the output
+    base = (size_t)bh * a.max_partitions;
+    stride = 1;
+  }
 
   __shared__ float red[4];
   __shared__ f32x4 part[PR][Q4];
 
   float mx = -INFINITY;
-  for (int i = tid; i < n_part; i += 256) mx = fmaxf(mx, m[i]);
+  for (int i = tid; i < n_rec; i += 256) mx = fmaxf(mx, a.ws_m[base + i * stride]);
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
   if (lane == 0) red[wave] = mx;
@@ -374,7 +563,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   __syncthreads();
 
   float sum = 0.f;
-  for (int i = tid; i < n_part; i += 256) sum = fmaf(l[i], exp2_fast(m[i] - M), sum);
+  for (int i = tid; i < n_rec; i += 256) {
+    const size_t rec = base + i * stride;
+    sum = fmaf(a.ws_l[rec], exp2_fast(a.ws_m[rec] - M), sum);
+  }
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) sum += __shfl_xor(sum, s);
   if (lane == 0) red[wave] = sum;
@@ -384,9 +576,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const int q = tid % Q4, pr = tid / Q4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int i = pr; i < n_part; i += PR) {
-    const float f = exp2_fast(m[i] - M);
-    acc += f * reinterpret_cast<const f32x4*>(o + (size_t)i * D)[q];
+  for (int i = pr; i < n_rec; i += PR) {
+    const size_t rec = base + i * stride;
+    const float f = exp2_fast(a.ws_m[rec] - M);
+    acc += f * reinterpret_cast<const f32x4*>(a.ws_o + rec * D)[q];
   }
   part[pr][q] = acc;
   __syncthreads();
@@ -400,23 +593,58 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   }
 }
 
-template <int DT, int D, int G>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.max_partitions, a.n_kv_heads, a.num_seqs);
-  hipLaunchKernelGGL((decode_kernel<DT, D, G>), grid, dim3(256), 0, stream, a);
+// Resident workgroups of a kernel on the current device (queried once per kernel).
+template <typename K>
+int resident_workgroups(K kernel, int threads) {
+  static int per_cu = -1;
+  if (per_cu < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+    per_cu = n;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 1;
+  return per_cu * cus;
+}
+
+template <int DT, int D, int G, int NW>
+hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
+  bool need_merge;
+  if (a.split) {
+    auto kernel = decode_split_kernel<DT, D, G, NW>;
+    a.split_workgroups = min(kSplitMaxWorkgroups, resident_workgroups(kernel, 64 * NW));
+    hipLaunchKernelGGL(kernel, dim3(a.split_workgroups), dim3(64 * NW), 0, stream, a);
+    need_merge = true;
+  } else {
+    const dim3 grid((a.n_kv_heads + NW - 1) / NW, a.max_partitions, a.num_seqs);
+    hipLaunchKernelGGL((decode_fixed_kernel<DT, D, G, NW>), grid, dim3(64 * NW), 0, stream, a);
+    need_merge = a.max_partitions > 1;
+  }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.max_partitions <= 1) return e;
-  hipLaunchKernelGGL((merge_kernel<DT, D>), dim3(a.num_seqs * a.n_heads), dim3(256), 0, stream, a);
+  if (e != hipSuccess || !need_merge) return e;
+  hipLaunchKernelGGL((merge_kernel<DT, D, NW>), dim3(a.num_seqs * a.n_heads), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int DT, int D, int G>
+hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
+  // Eight KV heads per workgroup when they divide evenly and the kernel fits 256 registers
+  // per lane (16-bit types, G <= 4); otherwise four (waves past the last head exit).
+  if constexpr (DT != 0 && G <= 4) {
+    if (max_waves_per_workgroup(a.n_kv_heads) == 8) return launch_typed<DT, D, G, 8>(a, stream);
+  }
+  return launch_typed<DT, D, G, 4>(a, stream);
 }
 
 template <int DT, int D>
 hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
   switch (group) {
-    case 1: return launch_typed<DT, D, 1>(a, stream);
-    case 2: return launch_typed<DT, D, 2>(a, stream);
-    case 4: return launch_typed<DT, D, 4>(a, stream);
-    case 8: return launch_typed<DT, D, 8>(a, stream);
+    case 1: return launch_waves<DT, D, 1>(a, stream);
+    case 2: return launch_waves<DT, D, 2>(a, stream);
+    case 4: return launch_waves<DT, D, 4>(a, stream);
+    case 8: return launch_waves<DT, D, 8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

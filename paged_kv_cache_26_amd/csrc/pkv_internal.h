@@ -8,8 +8,15 @@
 namespace pkv {
 
 constexpr int kBlockTokens = 16;   // tokens per KV block (the only supported block size)
-constexpr int kDecodeWaves = 4;    // waves per decode workgroup
-constexpr int kDefaultPartition = 512;
+constexpr int kFallbackPartition = 512;   // fixed partition size when the split mode cannot run
+constexpr int kSplitMaxSeqs = 4096;       // split mode keeps the per-sequence prefix in LDS
+constexpr int kSplitMaxWorkgroups = 1024; // upper bound of the split-mode grid
+constexpr int kSplitMinBlocks = 16;       // fewest blocks a split-mode workgroup is given
+
+// Waves per decode workgroup (one KV head each) used with this many KV heads. The
+// launcher may use fewer (4) for kernels that do not fit 256 registers per lane; this is
+// the upper bound the workspace is sized for.
+inline int max_waves_per_workgroup(int n_kv_heads) { return n_kv_heads % 8 == 0 ? 8 : 4; }
 
 struct AppendArgs {
   char* k_pool;
@@ -40,12 +47,17 @@ struct DecodeArgs {
   const char* v_pool;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_m;                       // [num_seqs, n_heads, max_partitions]
+  // Partial-result records (m, l, O[d_head]), fp32. Fixed mode: record
+  // (b * n_heads + h) * max_partitions + p. Split mode: see decode_split_kernel.
+  float* ws_m;
   float* ws_l;
-  float* ws_o;                       // [num_seqs, n_heads, max_partitions, d_head]
+  float* ws_o;
+  int32_t* ws_prefix;                // split mode: [num_seqs + 1] block prefix sums
   int32_t num_seqs, max_blocks_per_seq, num_blocks, max_context_len;
   int32_t n_heads, n_kv_heads;
-  int32_t partition_tokens, max_partitions;
+  int32_t split;                     // 1: balanced split over the GPU; 0: fixed partitions
+  int32_t partition_tokens, max_partitions;   // fixed mode
+  int32_t split_workgroups;          // split mode: grid size W (set by the launcher)
   float scale_log2;                  // scale * log2(e): scores are kept in base 2
 };
 

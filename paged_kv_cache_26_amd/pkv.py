@@ -31,7 +31,7 @@ _SIGNATURES = {
                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                             _c_i32, _c_i32, ctypes.c_float, _c_i32, _c_i32,
                                             _c_ptr, _c_size, _c_ptr]),
-    "pkv_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
+    "pkv_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_kv_bytes_per_token": (ctypes.c_int64, [_c_i32, _c_i32, _c_i32, _c_i32]),
     "pkv_gather_kv": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr]),
@@ -99,9 +99,9 @@ def pkv_kv_bytes_per_token(n_layers: int, n_kv_heads: int, d_head: int, dtype_by
     return int(load_library().pkv_kv_bytes_per_token(n_layers, n_kv_heads, d_head, dtype_bytes))
 
 
-def pkv_decode_workspace_bytes(num_seqs: int, n_heads: int, d_head: int, max_context_len: int,
-                               partition_tokens: int = 0) -> int:
-    return int(load_library().pkv_decode_workspace_bytes(num_seqs, n_heads, d_head,
+def pkv_decode_workspace_bytes(num_seqs: int, n_heads: int, n_kv_heads: int, d_head: int,
+                               max_context_len: int, partition_tokens: int = 0) -> int:
+    return int(load_library().pkv_decode_workspace_bytes(num_seqs, n_heads, n_kv_heads, d_head,
                                                          max_context_len, partition_tokens))
 
 
@@ -143,7 +143,7 @@ def pkv_paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_len
     B, H, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = pkv_decode_workspace_bytes(B, H, d, max_context_len, partition_tokens)
+    need = pkv_decode_workspace_bytes(B, H, k_pool.shape[2], d, max_context_len, partition_tokens)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

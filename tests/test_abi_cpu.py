@@ -50,15 +50,28 @@ def test_kv_bytes_per_token(lib):
 
 
 def test_workspace_bytes(lib):
-    # one partition: no workspace
-    assert pkv.pkv_decode_workspace_bytes(4, 4, 64, 101, 0) == 0
-    assert pkv.pkv_decode_workspace_bytes(4, 4, 64, 512, 0) == 0
-    # 131073 tokens at 512 per partition: 257 partitions
-    rows = 4 * 32 * 257
     al = lambda x: (x + 255) // 256 * 256
-    assert pkv.pkv_decode_workspace_bytes(4, 32, 128, 131073, 0) == 2 * al(rows * 4) + al(rows * 128 * 4)
-    assert pkv.pkv_decode_workspace_bytes(4, 32, 128, 131073, 100) == 0      # invalid partition
-    assert pkv.pkv_decode_workspace_bytes(0, 32, 128, 131073, 0) == 0
+    ws = pkv.pkv_decode_workspace_bytes
+    # fixed partitions: nothing when every sequence fits one partition
+    assert ws(4, 4, 4, 64, 101, 512) == 0
+    assert ws(4, 4, 4, 64, 512, 512) == 0
+    # 131073 tokens at 512 per partition: 257 partitions per (sequence, head)
+    rows = 4 * 32 * 257
+    assert ws(4, 32, 8, 128, 131073, 512) == 2 * al(rows * 4) + al(rows * 128 * 4)
+    # balanced split (partition 0): prefix sums + (1024 + ceil(8/8) * 4) * 8 * 4 records
+    rec = (1024 + 4) * 8 * 4
+    assert ws(4, 32, 8, 128, 131073, 0) == al(5 * 4) + 2 * al(rec * 4) + al(rec * 128 * 4)
+    # four KV heads: four waves per workgroup
+    rec = (1024 + 1 * 4) * 4 * 1
+    assert ws(4, 4, 4, 64, 600, 0) == al(5 * 4) + 2 * al(rec * 4) + al(rec * 64 * 4)
+    # every sequence within one 512-token partition: a single kernel, no workspace
+    assert ws(4, 4, 4, 64, 101, 0) == 0
+    # more sequences than the split mode holds: fixed 512-token partitions
+    rows = 5000 * 8 * 2
+    assert ws(5000, 8, 8, 64, 1000, 0) == 2 * al(rows * 4) + al(rows * 64 * 4)
+    assert ws(4, 32, 8, 128, 131073, 100) == 0      # invalid partition
+    assert ws(0, 32, 8, 128, 131073, 0) == 0
+    assert ws(4, 32, 6, 128, 131073, 0) == 0        # 32 query heads over 6 KV heads
 
 
 def test_status_strings(lib):
@@ -89,6 +102,7 @@ def _decode_call(lib, **over):
     (dict(maxctx=0), -7), (dict(maxctx=8 * 16 + 1), -7),
     (dict(P=24), -8), (dict(P=-16), -8),
     (dict(maxctx=128, P=16), -9),                      # 8 partitions need a workspace
+    (dict(maxctx=600, mbps=64), -9),                   # the balanced split needs one
     (dict(q=0x20004), -11),
     (dict(out=0x100000), -12),                         # out inside k_pool
     (dict(scale=float("nan")), -2),

@@ -145,7 +145,7 @@ def test_decode_parity_other_shapes(dtype, d, H, Hkv):
 def test_partition_size_invariance_fp32():
     """Different partition sizes only reorder fp32 sums."""
     wl = _custom_f32_workload()
-    outs = {p: _gpu_step(wl, p)[0] for p in (16, 128, 256, 512, 1024, 2048)}
+    outs = {p: _gpu_step(wl, p)[0] for p in (0, 16, 128, 256, 512, 1024, 2048)}
     base = outs[2048]                      # one partition per sequence: no merge
     for p, o in outs.items():
         rel = np.linalg.norm(o - base) / np.linalg.norm(base)
@@ -247,14 +247,55 @@ def test_needle_output_is_order_one():
     assert_close(got, ref, "bf16", "needle")
 
 
-def test_swapped_table_entry_is_detected():
-    """Negative control: a wrong table on the GPU side must fail the parity check."""
+def test_wrong_table_entry_is_detected():
+    """Negative control: a table entry pointing at another sequence's block must fail.
+
+    (Swapping two entries of one sequence would only reorder its tokens, which attention
+    does not see.)
+    """
+    wl = wlm.make_workload(3, small=True)
+    ref = _oracle_out(wl, ("small", 3))
+    b = int(np.argmin(wl.context_lens))
+    other = (b + 1) % wl.batch
+    t = wlm.to_torch(wl, DEV)
+    t["block_tables"][b, 1] = t["block_tables"][other, 1].clone()
+    got, _, _ = _gpu_step(wl, 0, t)
+    assert not within(got[b], ref[b], "bf16")[0]
+    keep = [i for i in range(wl.batch) if i != b]
+    assert within(got[keep], ref[keep], "bf16")[0]      # the other sequences are unaffected
+
+
+# ---------------------------------------------------------------------------------------
+# Device-side bad values: the kernels stay in bounds and flag the sequence with NaN
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ptok", [0, 128])
+def test_invalid_context_length_gives_nan_for_that_sequence_only(ptok):
     wl = wlm.make_workload(3, small=True)
     ref = _oracle_out(wl, ("small", 3))
     t = wlm.to_torch(wl, DEV)
-    tab = t["block_tables"]
-    tab[0, 0], tab[0, 1] = tab[0, 1].clone(), tab[0, 0].clone()
-    got, _, _ = _gpu_step(wl, 0, t)
-    assert not within(got, ref, "bf16")[0]
-    # the other sequences are unaffected
-    assert within(got[1:], ref[1:], "bf16")[0]
+    pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                      t["positions"])
+    t["context_lens"][1] = 0
+    t["context_lens"][4] = wl.max_context_len + 1
+    out = torch.empty_like(t["q"])
+    pkv.pkv_paged_decode_attention(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                                   t["context_lens"], wl.max_context_len, wl.scale,
+                                   partition_tokens=ptok)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy()
+    assert np.isnan(got[1]).all() and np.isnan(got[4]).all()
+    keep = [0, 2, 3, 5]
+    assert_close(got[keep], ref[keep], "bf16", f"P {ptok}")
+
+
+@pytest.mark.parametrize("ptok", [0, 128])
+def test_out_of_range_table_entry_gives_nan_for_that_sequence_only(ptok):
+    wl = wlm.make_workload(3, small=True)
+    ref = _oracle_out(wl, ("small", 3))
+    t = wlm.to_torch(wl, DEV)
+    t["block_tables"][2, 3] = wl.num_blocks + 7
+    got, _, _ = _gpu_step(wl, ptok, t)
+    assert np.isnan(got[2]).all()
+    keep = [0, 1, 3, 4, 5]
+    assert_close(got[keep], ref[keep], "bf16", f"P {ptok}")
