@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a buffer of this many MiB 3 times (a dispatch of "
                          "known traffic for scaling hardware byte counters)")
+    ap.add_argument("--component", choices=["decode", "block-manager"], default="decode",
+                    help="decode: the decode step (default); block-manager: the native block "
+                         "manager and the copy-on-write block copy")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     return ap.parse_args()
@@ -239,6 +242,109 @@ def cpu_baseline(wl, target_s: float) -> dict:
     }
 
 
+def run_block_manager(args) -> dict:
+    """Native block manager on the shared-prefix batch shape, and the GPU block copy.
+
+    Host: 8 groups x 16 sequences forked from a 2048-token prefix; a step reserves the
+    next token's slot for all 128 sequences with one batched call (the prefix is block
+    aligned, so no copy; 1 step in 16 opens a new block per sequence). Timed against the
+    reference manager of the workload module doing the same operations one by one.
+    GPU: copy 2048 random 32 KiB blocks in both pools (128 MiB read + 128 MiB written).
+    """
+    import torch
+
+    from paged_kv_cache_26_amd import pkv
+    from paged_kv_cache_26_amd import workload as wlm
+    from paged_kv_cache_26_amd.block_manager import NativeBlockManager
+
+    groups, per_group, prefix, steps = 8, 16, 2048, 1024
+    n_blocks = groups * 128 + groups * per_group * (steps // 16 + 1)
+
+    def drive(mgr, append):
+        for g in range(groups):
+            mgr.add_sequence(-1 - g)
+            mgr.grow(-1 - g, prefix)
+            for i in range(per_group):
+                mgr.fork(-1 - g, g * per_group + i)
+        t0 = time.perf_counter()
+        for t in range(prefix, prefix + steps):
+            for sq in range(groups * per_group):
+                append(mgr, sq, t)
+        return time.perf_counter() - t0
+
+    nat = NativeBlockManager(n_blocks, 16)
+    seqs = np.arange(groups * per_group, dtype=np.int64)
+    for g in range(groups):
+        nat.add_sequence(-1 - g)
+        nat.grow(-1 - g, prefix)
+        for i in range(per_group):
+            nat.fork(-1 - g, g * per_group + i)
+    # one C call per step on buffers prepared once (as a native scheduler would call it)
+    import ctypes
+    toks = np.empty(len(seqs), dtype=np.int32)
+    blocks = np.empty(len(seqs), dtype=np.int32)
+    slots = np.empty(len(seqs), dtype=np.int32)
+    pairs_h = np.empty((len(seqs), 2), dtype=np.int32)
+    done = ctypes.c_int32(0)
+    ptr = lambda a: ctypes.c_void_p(a.ctypes.data)
+    p_seqs, p_toks, p_blk, p_slot, p_pairs = map(ptr, (seqs, toks, blocks, slots, pairs_h))
+    fn, handle, n_seq = nat._lib.pkv_bm_append_slots, nat._h, len(seqs)
+    t0 = time.perf_counter()
+    for t in range(prefix, prefix + steps):
+        toks.fill(t)
+        if fn(handle, p_seqs, p_toks, n_seq, p_blk, p_slot, p_pairs, ctypes.byref(done)) != 0:
+            raise RuntimeError("block manager ran out of blocks")
+    t_nat = time.perf_counter() - t0
+
+    def ref_append(m, sq, t):
+        m.grow(sq, t + 1)
+        m.make_writable(sq, t // 16)
+
+    t_ref = drive(wlm.BlockManager(n_blocks, 16), ref_append)
+    appends = steps * groups * per_group
+
+    pkv.load_library()
+    dev = torch.device("cuda:0")
+    nb, hkv, d = 8192, 8, 128
+    kp = torch.empty((nb, 16, hkv, d), dtype=torch.bfloat16, device=dev).normal_()
+    vp = torch.empty_like(kp).normal_()
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(nb)
+    pairs = torch.from_numpy(np.stack([perm[:2048], perm[2048:4096]], 1).astype(np.int32)).to(dev)
+    for _ in range(args.warmup):
+        pkv.pkv_copy_blocks(kp, vp, pairs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        pkv.pkv_copy_blocks(kp, vp, pairs)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    moved = 2 * 2 * 2048 * 16 * hkv * d * 2          # K and V, read and write
+    gbps = moved / (ms * 1e-3) / 1e9
+    return {
+        "metric": "block manager: slot reservations per second (host); copy-on-write block "
+                  "copy GB/s (GPU)",
+        "value": round(appends / t_nat, 1),
+        "unit": "appends/s",
+        "higher_is_better": True,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "config": {"workload": "shared-prefix batch: 8 groups x 16 sequences, 2048-token prefix, "
+                               f"{steps} decode steps of slot reservations"},
+        "host": {"native_us_per_step": round(t_nat / steps * 1e6, 2),
+                 "reference_python_us_per_step": round(t_ref / steps * 1e6, 2),
+                 "speedup_vs_reference": round(t_ref / t_nat, 1)},
+        "copy_blocks": {"blocks": 2048, "block_bytes": 16 * hkv * d * 2, "us": round(ms * 1e3, 2),
+                        "GB_per_s": round(gbps, 1),
+                        "roofline": {"bound": "hbm", "achieved": round(gbps, 1),
+                                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                     "frac": round(gbps / HBM_PEAK_GBPS, 4)}},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -247,6 +353,9 @@ def main():
     if os.environ.get("WORLD_SIZE", "1") != "1":
         print("this build runs on one GPU only", file=sys.stderr)
         sys.exit(2)
+    if args.component == "block-manager":
+        print(json.dumps(run_block_manager(args)), flush=True)
+        return
     cfgs = [1, 2, 3, 4, 5] if args.all else [args.config]
     for cfg in cfgs:
         res = run_config(args, cfg, want_cpu=not args.no_cpu_baseline)

@@ -2,6 +2,7 @@
 // The operations and their sources are documented in include/pkv.h.
 
 #include "../../include/pkv.h"
+#include "../../include/pkv_block_manager.h"
 
 #include <cmath>
 
@@ -102,6 +103,10 @@ const char* pkv_status_str(int32_t status) {
     case PKV_ERR_LAUNCH: return "kernel launch failed";
     case PKV_ERR_ALIGN: return "device pointers must be 16-byte aligned";
     case PKV_ERR_ALIAS: return "out overlaps an input";
+    case PKV_ERR_OUT_OF_BLOCKS: return "not enough free blocks in the pool";
+    case PKV_ERR_NO_SEQUENCE: return "unknown sequence id";
+    case PKV_ERR_SEQUENCE_EXISTS: return "sequence id already in use";
+    case PKV_ERR_BAD_BLOCK: return "block id outside the pool";
     default: return "unknown status";
   }
 }

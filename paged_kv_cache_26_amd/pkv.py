@@ -36,6 +36,23 @@ _SIGNATURES = {
     "pkv_gather_kv": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr]),
     "pkv_status_str": (ctypes.c_char_p, [_c_i32]),
+    # block manager (include/pkv_block_manager.h)
+    "pkv_bm_create": (_c_ptr, [_c_i32, _c_i32, _c_ptr]),
+    "pkv_bm_destroy": (None, [_c_ptr]),
+    "pkv_bm_add_sequence": (_c_i32, [_c_ptr, ctypes.c_int64]),
+    "pkv_bm_fork": (_c_i32, [_c_ptr, ctypes.c_int64, ctypes.c_int64]),
+    "pkv_bm_free_sequence": (_c_i32, [_c_ptr, ctypes.c_int64]),
+    "pkv_bm_grow": (_c_i32, [_c_ptr, ctypes.c_int64, _c_i32]),
+    "pkv_bm_append_slot": (_c_i32, [_c_ptr, ctypes.c_int64, _c_i32, _c_ptr, _c_ptr, _c_ptr,
+                                    _c_ptr]),
+    "pkv_bm_append_slots": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_ptr, _c_ptr,
+                                     _c_ptr]),
+    "pkv_bm_num_free": (_c_i32, [_c_ptr]),
+    "pkv_bm_refcount": (_c_i32, [_c_ptr, _c_i32]),
+    "pkv_bm_num_blocks_of": (_c_i32, [_c_ptr, ctypes.c_int64]),
+    "pkv_bm_tables": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_ptr]),
+    "pkv_copy_blocks": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                 _c_i32, _c_ptr]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -170,6 +187,19 @@ def pkv_gather_kv(k_out, v_out, k_pool, v_pool, block_tables, context_lens,
                            _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_gather_kv")
+
+
+def pkv_copy_blocks(k_pool, v_pool, pairs, stream=None) -> None:
+    """pool[dst] = pool[src] in both pools for every row (src, dst) of pairs [n, 2] int32."""
+    lib = load_library()
+    _check_device(k_pool, v_pool, pairs)
+    _require(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2,
+             "pairs must be int32 [n, 2]")
+    st = lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0],
+                             k_pool.shape[0], k_pool.shape[1], k_pool.shape[2], k_pool.shape[3],
+                             _DTYPE_CODE[k_pool.dtype], _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_copy_blocks")
 
 
 # short names used in the pages' statement of the problem
