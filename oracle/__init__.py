@@ -14,6 +14,7 @@ from .pkv_oracle import (  # noqa: F401
     online_softmax_attention,
     online_softmax_partial,
     paged_decode_attention,
+    paged_multi_query_attention,
     read_kv,
     softmax_two_pass,
     storage_to_f64,

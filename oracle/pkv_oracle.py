@@ -246,3 +246,49 @@ def online_softmax_attention(q_vec: np.ndarray, keys: np.ndarray, vals: np.ndarr
                                     vals[s:s + partition_tokens], scale, tile_tokens)
              for s in range(0, keys.shape[0], partition_tokens)]
     return merge_partitions([p[0] for p in parts], [p[1] for p in parts], [p[2] for p in parts])
+
+
+# --------------------------------------------------------------------------------------
+# Several new tokens per sequence ("09-inference-optimization", section KV Cache: with
+# seq_len > 1 new tokens the scores get a causal mask — key k is hidden from new query i
+# when k > K - seq_len + i, K counting every cached token; speculative verification checks
+# k drafted tokens in one pass of the target model: "LLM推理与服务：面试问题与推荐回答" Q9,
+# "Scaling Book 第 11 章" §11.7).
+# --------------------------------------------------------------------------------------
+
+def paged_multi_query_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                                block_tables: np.ndarray, context_lens: np.ndarray,
+                                block_size: int, scale: float, dtype: str,
+                                pairs=None) -> np.ndarray:
+    """fp64 outputs for q_len new query tokens per sequence, causally masked.
+
+    q:            [B, q_len, n_heads, d_head] stored dtype.
+    context_lens: [B] cached tokens INCLUDING the q_len new ones (N_b >= q_len).
+    New query i (0-based) of sequence b sees tokens 0 .. N_b - q_len + i.
+    pairs:        optional iterable of (b, i, h) to compute; others stay NaN.
+    Returns [B, q_len, n_heads, d_head] fp64.
+    """
+    B, q_len, n_heads, d_head = q.shape
+    n_kv_heads = k_pool.shape[2]
+    if n_heads % n_kv_heads:
+        raise ValueError("n_heads must be a multiple of n_kv_heads")
+    group = n_heads // n_kv_heads
+    out = np.full((B, q_len, n_heads, d_head), np.nan, dtype=np.float64)
+    wanted = {}
+    if pairs is None:
+        pairs = [(b, i, h) for b in range(B) for i in range(q_len) for h in range(n_heads)]
+    for b, i, h in pairs:
+        wanted.setdefault((int(b), int(h) // group), []).append((int(i), int(h)))
+    for (b, j) in sorted(wanted):
+        n_tok = int(context_lens[b])
+        if n_tok < q_len:
+            raise ValueError("every sequence holds at least its q_len new tokens")
+        keys = storage_to_f64(gather_kv(k_pool, block_tables[b], n_tok, block_size, j), dtype)
+        vals = storage_to_f64(gather_kv(v_pool, block_tables[b], n_tok, block_size, j), dtype)
+        for i, h in sorted(set(wanted[(b, j)])):
+            visible = n_tok - q_len + i + 1                  # causal limit of query i
+            qh = storage_to_f64(q[b, i, h], dtype)
+            scores = scale * (keys[:visible] @ qh)
+            weights = softmax_two_pass(scores)
+            out[b, i, h] = weights @ vals[:visible]
+    return out

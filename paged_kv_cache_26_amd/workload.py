@@ -15,7 +15,8 @@ Workload recipe (the same recipe is stated in the design notes):
 * every slot and block not holding a token is filled with NaN ("poison"), so a kernel
   that reads outside a sequence's used slots produces NaN.
 * "context length" in a workload description is the length L_b *before* the decode step.
-  The step appends one token at position L_b, then attends over N_b = L_b + 1 tokens.
+  The step appends one token at position L_b (q_len tokens at L_b .. L_b + q_len - 1 for
+  multi-query steps), then attends over N_b = L_b + q_len tokens.
 
 The block manager follows the paging scheme of "LLM 推理优化全景实战" §2.3 (a shared pool
 of fixed-size blocks, a per-request table from logical to physical block, allocation on
@@ -207,6 +208,7 @@ class Spec:
     prefix_len: int = 0
     suffix_range: tuple | None = None  # per-sequence suffix ~ U{lo..hi}
     block_size: int = BLOCK_SIZE
+    q_len: int = 1                     # new tokens (queries) per sequence this step
 
     @property
     def group(self) -> int:
@@ -253,10 +255,10 @@ class Workload:
     k_pool: np.ndarray          # [num_blocks, block_size, n_kv_heads, d_head], before append
     v_pool: np.ndarray
     block_tables: np.ndarray    # [B, max_blocks_per_seq] int32, unused = -1
-    positions: np.ndarray       # [B] int32, L_b (where the new token goes)
-    context_lens: np.ndarray    # [B] int32, N_b = L_b + 1
-    q: np.ndarray               # [B, n_heads, d_head]
-    k_new: np.ndarray           # [B, n_kv_heads, d_head]
+    positions: np.ndarray       # [B] int32, L_b (where the first new token goes)
+    context_lens: np.ndarray    # [B] int32, N_b = L_b + q_len
+    q: np.ndarray               # [B, n_heads, d_head] ([B, q_len, n_heads, d_head] if q_len > 1)
+    k_new: np.ndarray           # [B, n_kv_heads, d_head] ([B, q_len, n_kv_heads, d_head] if q_len > 1)
     v_new: np.ndarray
     refcount: np.ndarray
     shared_tokens: int          # tokens counted more than once across sequences
@@ -350,11 +352,11 @@ def _allocate(mgr: BlockManager, spec: Spec, ctx_before, prefix_of):
         if spec.groups:
             mgr.fork(parents[prefix_of[b]], b)
             first_private = spec.prefix_len // spec.block_size
-            if spec.prefix_len % spec.block_size and ctx_before[b] + 1 > spec.prefix_len:
+            if spec.prefix_len % spec.block_size and ctx_before[b] + spec.q_len > spec.prefix_len:
                 mgr.make_writable(b, first_private)
         else:
             mgr.add_sequence(b)
-        mgr.grow(b, ctx_before[b] + 1)
+        mgr.grow(b, ctx_before[b] + spec.q_len)
     if spec.groups:
         for g in range(spec.groups):
             mgr.free_sequence(parents[g])
@@ -460,13 +462,15 @@ def make_workload(spec: Spec | int, seed: int | None = None, *, keep_logical: bo
                 logical_v.append(vv)
 
     # 4. query, 5. new token's K and V
-    q = to_storage(_draw(rng, (B, spec.n_heads, d), spec.dist, "q"), spec.dtype)
-    k_new = to_storage(_draw(rng, (B, Hkv, d), spec.dist, "k"), spec.dtype)
-    v_new = to_storage(_draw(rng, (B, Hkv, d), spec.dist, "v"), spec.dtype)
+    ql = spec.q_len
+    lead = (B,) if ql == 1 else (B, ql)
+    q = to_storage(_draw(rng, lead + (spec.n_heads, d), spec.dist, "q"), spec.dtype)
+    k_new = to_storage(_draw(rng, lead + (Hkv, d), spec.dist, "k"), spec.dtype)
+    v_new = to_storage(_draw(rng, lead + (Hkv, d), spec.dist, "v"), spec.dtype)
 
     positions = np.asarray(ctx, dtype=np.int32)
     return Workload(spec=spec, seed=seed, k_pool=k_pool, v_pool=v_pool, block_tables=tables,
-                    positions=positions, context_lens=positions + 1, q=q, k_new=k_new,
+                    positions=positions, context_lens=positions + ql, q=q, k_new=k_new,
                     v_new=v_new, refcount=mgr.refcount_array(), shared_tokens=shared_tokens,
                     logical_k=logical_k, logical_v=logical_v)
 
