@@ -66,7 +66,8 @@ enum pkv_status {
   PKV_ERR_WORKSPACE = -9,   /* workspace is NULL or smaller than pkv_decode_workspace_bytes */
   PKV_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch */
   PKV_ERR_ALIGN = -11,      /* a device pointer is not 16-byte aligned */
-  PKV_ERR_ALIAS = -12       /* out overlaps q, k_pool or v_pool */
+  PKV_ERR_ALIAS = -12,      /* out overlaps q, k_pool or v_pool */
+  PKV_ERR_QUERIES = -17     /* q_len < 1 or q_len * (n_heads / n_kv_heads) > 16 */
 };
 
 /*
@@ -94,6 +95,18 @@ int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void*
                       int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
                       int32_t block_size, int32_t n_kv_heads, int32_t d_head, int32_t dtype,
                       hipStream_t stream);
+
+/*
+ * pkv_kv_append_tokens - pkv_kv_append for n_tokens (1..16) consecutive new tokens per
+ * sequence: token i of sequence b (k_new/v_new [num_seqs, n_tokens, n_kv_heads, d_head])
+ * goes to position positions[b] + i. The blocks of every written position must be in the
+ * table already. Same copy rule and error behaviour as pkv_kv_append.
+ */
+int32_t pkv_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                             const int32_t* block_tables, const int32_t* positions,
+                             int32_t num_seqs, int32_t n_tokens, int32_t max_blocks_per_seq,
+                             int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                             int32_t d_head, int32_t dtype, hipStream_t stream);
 
 /*
  * pkv_paged_decode_attention - one query token per sequence attends to its paged
@@ -158,6 +171,40 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
 size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads,
                                   int32_t d_head, int32_t max_context_len,
                                   int32_t partition_tokens);
+
+/*
+ * pkv_paged_multi_query_attention - q_len new query tokens per sequence attend to the
+ * paged context under a causal mask (speculative verification of q_len drafted tokens,
+ * or a short chunk of new tokens).
+ *
+ * Source: "09-inference-optimization" KV Cache (with seq_len > 1 new tokens, key k is
+ * hidden from new query i when k > K - seq_len + i, K counting all cached tokens);
+ * "LLM推理与服务：面试问题与推荐回答" Q9 and "Scaling Book 第 11 章" §11.7 (the target model
+ * checks all drafted tokens in one pass).
+ *
+ *   out, q          [num_seqs, q_len, n_heads, d_head], dtype.
+ *   context_lens    N_b, INCLUDING the q_len new tokens (append them first, e.g. with
+ *                   pkv_kv_append_tokens); new query i sees tokens 0 .. N_b - q_len + i.
+ *                   q_len <= N_b <= max_context_len, else NaN outputs for that sequence.
+ *   q_len           1 .. 16 / (n_heads / n_kv_heads).
+ * Everything else as pkv_paged_decode_attention (q_len = 1 gives exactly its result);
+ * workspace size from pkv_multi_query_workspace_bytes.
+ */
+int32_t pkv_paged_multi_query_attention(void* out, const void* q, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t q_len, int32_t max_blocks_per_seq,
+                                        int32_t num_blocks, int32_t max_context_len,
+                                        int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+                                        int32_t d_head, float scale, int32_t partition_tokens,
+                                        int32_t dtype, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
+/* Scratch bytes of pkv_paged_multi_query_attention (host only); the records of
+ * pkv_decode_workspace_bytes times q_len. 0 for invalid sizes. */
+size_t pkv_multi_query_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t n_heads,
+                                       int32_t n_kv_heads, int32_t d_head,
+                                       int32_t max_context_len, int32_t partition_tokens);
 
 /*
  * pkv_kv_bytes_per_token - bytes one token occupies in the KV cache of a whole model:

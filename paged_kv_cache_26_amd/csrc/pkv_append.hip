@@ -12,20 +12,22 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// grid (num_seqs, 2): y = 0 writes K, y = 1 writes V. One thread per 16-byte chunk.
+// grid (num_seqs, 2 * n_tokens): y = 2i writes K, y = 2i + 1 writes V of new token i,
+// which goes to position positions[b] + i. One thread per 16-byte chunk.
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int b = blockIdx.x;
-  const int t = a.positions[b];
+  const int i = blockIdx.y >> 1, which = blockIdx.y & 1;
+  const int t = a.positions[b] + i;
   const int logical = t >> 4;
   if (t < 0 || logical >= a.max_blocks_per_seq) return;
   const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + logical];
   if ((unsigned)phys >= (unsigned)a.num_blocks) return;
   const size_t slot_row = (size_t)phys * kBlockTokens + (t & 15);
-  char* dst = (blockIdx.y == 0 ? a.k_pool : a.v_pool) + slot_row * a.row_bytes;
-  const char* src = (blockIdx.y == 0 ? a.k_new : a.v_new) + (size_t)b * a.row_bytes;
+  char* dst = (which == 0 ? a.k_pool : a.v_pool) + slot_row * a.row_bytes;
+  const char* src = (which == 0 ? a.k_new : a.v_new) + ((size_t)b * a.n_tokens + i) * a.row_bytes;
   const int chunks = a.row_bytes >> 4;
-  for (int i = threadIdx.x; i < chunks; i += blockDim.x)
-    reinterpret_cast<u32x4*>(dst)[i] = reinterpret_cast<const u32x4*>(src)[i];
+  for (int k = threadIdx.x; k < chunks; k += blockDim.x)
+    reinterpret_cast<u32x4*>(dst)[k] = reinterpret_cast<const u32x4*>(src)[k];
 }
 
 // grid (blocks of max_context_len, num_seqs): copies the used rows of one block.
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int chunks = a.row_bytes >> 4;
   const int threads = chunks < 256 ? ((chunks + 63) & ~63) : 256;
-  hipLaunchKernelGGL(append_kernel, dim3(a.num_seqs, 2), dim3(threads), 0, stream, a);
+  hipLaunchKernelGGL(append_kernel, dim3(a.num_seqs, 2 * a.n_tokens), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -39,8 +39,8 @@ struct Plan {
   size_t bytes;          // total workspace bytes
 };
 
-Plan make_plan(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads, int32_t d_head,
-               int32_t max_context_len, int32_t partition_tokens) {
+Plan make_plan(int32_t num_seqs, int32_t q_len, int32_t n_heads, int32_t n_kv_heads,
+               int32_t d_head, int32_t max_context_len, int32_t partition_tokens) {
   Plan p{};
   // 0 selects the balanced split, except when every sequence fits one 512-token partition
   // (one kernel, no merge) or there are more sequences than the split mode holds.
@@ -50,12 +50,12 @@ Plan make_plan(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads, int32_t d_
     const int64_t nw = pkv::max_waves_per_workgroup(n_kv_heads);
     const int64_t hg = (n_kv_heads + nw - 1) / nw;
     const int64_t g = n_heads / n_kv_heads;
-    p.records = (size_t)((pkv::kSplitMaxWorkgroups + hg * num_seqs) * nw * g);
+    p.records = (size_t)((pkv::kSplitMaxWorkgroups + hg * num_seqs) * nw * g * q_len);
     p.prefix_ints = (size_t)num_seqs + 1;
   } else {
     p.partition = partition_tokens == 0 ? pkv::kFallbackPartition : partition_tokens;
     p.parts = ((int64_t)max_context_len + p.partition - 1) / p.partition;
-    p.records = p.parts > 1 ? (size_t)num_seqs * n_heads * (size_t)p.parts : 0;
+    p.records = p.parts > 1 ? (size_t)num_seqs * q_len * n_heads * (size_t)p.parts : 0;
   }
   if (p.records > 0)
     p.bytes = align256(p.prefix_ints * sizeof(int32_t)) + 2 * align256(p.records * sizeof(float)) +
@@ -84,6 +84,73 @@ int32_t check_pool_args(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t nu
   return PKV_OK;
 }
 
+bool valid_q_len(int32_t q_len, int32_t n_heads, int32_t n_kv_heads) {
+  return q_len >= 1 && n_kv_heads > 0 && q_len * (n_heads / n_kv_heads) <= 16;
+}
+
+// Shared by the single- and multi-query entry points.
+int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t q_len, int32_t max_blocks_per_seq, int32_t num_blocks,
+                    int32_t max_context_len, int32_t block_size, int32_t n_heads,
+                    int32_t n_kv_heads, int32_t d_head, float scale, int32_t partition_tokens,
+                    int32_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
+  int32_t st = check_pool_args(num_seqs, max_blocks_per_seq, num_blocks, max_context_len,
+                               block_size, n_kv_heads, d_head, dtype);
+  if (st != PKV_OK) return st;
+  if (!valid_group(n_heads, n_kv_heads)) return PKV_ERR_GROUP;
+  if (!valid_q_len(q_len, n_heads, n_kv_heads)) return PKV_ERR_QUERIES;
+  if (max_context_len < q_len) return PKV_ERR_CONTEXT;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (partition_tokens < 0 || partition_tokens % pkv::kBlockTokens) return PKV_ERR_PARTITION;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_ERR_ALIGN;
+  const size_t eb = (size_t)elem_bytes(dtype);
+  const size_t out_bytes = (size_t)num_seqs * q_len * n_heads * d_head * eb;
+  const size_t pool_bytes = (size_t)num_blocks * pkv::kBlockTokens * n_kv_heads * d_head * eb;
+  if (overlaps(out, out_bytes, q, out_bytes) || overlaps(out, out_bytes, k_pool, pool_bytes) ||
+      overlaps(out, out_bytes, v_pool, pool_bytes))
+    return PKV_ERR_ALIAS;
+
+  const Plan plan = make_plan(num_seqs, q_len, n_heads, n_kv_heads, d_head, max_context_len,
+                              partition_tokens);
+  if (!plan.split && plan.parts > 65535) return PKV_ERR_PARTITION;   // grid y limit
+  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned16(workspace)))
+    return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = static_cast<const char*>(k_pool);
+  a.v_pool = static_cast<const char*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.n_heads = n_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.q_len = q_len;
+  a.split = plan.split ? 1 : 0;
+  a.partition_tokens = plan.partition;
+  a.max_partitions = (int32_t)plan.parts;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+  if (plan.bytes > 0) {
+    char* ws = static_cast<char*>(workspace);
+    const size_t pre = align256(plan.prefix_ints * sizeof(int32_t));
+    const size_t vec = align256(plan.records * sizeof(float));
+    a.ws_prefix = plan.prefix_ints ? reinterpret_cast<int32_t*>(ws) : nullptr;
+    a.ws_m = reinterpret_cast<float*>(ws + pre);
+    a.ws_l = reinterpret_cast<float*>(ws + pre + vec);
+    a.ws_o = reinterpret_cast<float*>(ws + pre + 2 * vec);
+  }
+  const hipError_t e = pkv::launch_decode(a, dtype, d_head, n_heads / n_kv_heads, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -107,6 +174,7 @@ const char* pkv_status_str(int32_t status) {
     case PKV_ERR_NO_SEQUENCE: return "unknown sequence id";
     case PKV_ERR_SEQUENCE_EXISTS: return "sequence id already in use";
     case PKV_ERR_BAD_BLOCK: return "block id outside the pool";
+    case PKV_ERR_QUERIES: return "q_len must be >= 1 with q_len * (n_heads / n_kv_heads) <= 16";
     default: return "unknown status";
   }
 }
@@ -124,20 +192,20 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_k
       !valid_group(n_heads, n_kv_heads) || partition_tokens < 0 ||
       partition_tokens % pkv::kBlockTokens)
     return 0;
-  return make_plan(num_seqs, n_heads, n_kv_heads, d_head, max_context_len, partition_tokens).bytes;
+  return make_plan(num_seqs, 1, n_heads, n_kv_heads, d_head, max_context_len, partition_tokens).bytes;
 }
 
-int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
-                      const int32_t* block_tables, const int32_t* positions,
-                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
-                      int32_t block_size, int32_t n_kv_heads, int32_t d_head, int32_t dtype,
-                      hipStream_t stream) {
+int32_t pkv_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                             const int32_t* block_tables, const int32_t* positions,
+                             int32_t num_seqs, int32_t n_tokens, int32_t max_blocks_per_seq,
+                             int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                             int32_t d_head, int32_t dtype, hipStream_t stream) {
   if (!k_pool || !v_pool || !k_new || !v_new || !block_tables || !positions) return PKV_ERR_NULL;
   if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
   if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
   if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
   if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
-      n_kv_heads <= 0)
+      n_kv_heads <= 0 || n_tokens < 1 || n_tokens > 16)
     return PKV_ERR_SHAPE;
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
     return PKV_ERR_ALIGN;
@@ -149,10 +217,21 @@ int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void*
   a.block_tables = block_tables;
   a.positions = positions;
   a.num_seqs = num_seqs;
+  a.n_tokens = n_tokens;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.num_blocks = num_blocks;
   a.row_bytes = n_kv_heads * d_head * elem_bytes(dtype);
   return pkv::launch_append(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void* v_new,
+                      const int32_t* block_tables, const int32_t* positions,
+                      int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                      int32_t block_size, int32_t n_kv_heads, int32_t d_head, int32_t dtype,
+                      hipStream_t stream) {
+  return pkv_kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, positions, num_seqs, 1,
+                              max_blocks_per_seq, num_blocks, block_size, n_kv_heads, d_head,
+                              dtype, stream);
 }
 
 int32_t pkv_gather_kv(void* k_out, void* v_out, const void* k_pool, const void* v_pool,
@@ -191,56 +270,36 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
                                    float scale, int32_t partition_tokens, int32_t dtype,
                                    void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
-  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
-  int32_t st = check_pool_args(num_seqs, max_blocks_per_seq, num_blocks, max_context_len,
-                               block_size, n_kv_heads, d_head, dtype);
-  if (st != PKV_OK) return st;
-  if (!valid_group(n_heads, n_kv_heads)) return PKV_ERR_GROUP;
-  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
-  if (partition_tokens < 0 || partition_tokens % pkv::kBlockTokens) return PKV_ERR_PARTITION;
-  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
-    return PKV_ERR_ALIGN;
-  const size_t eb = (size_t)elem_bytes(dtype);
-  const size_t out_bytes = (size_t)num_seqs * n_heads * d_head * eb;
-  const size_t pool_bytes = (size_t)num_blocks * pkv::kBlockTokens * n_kv_heads * d_head * eb;
-  if (overlaps(out, out_bytes, q, out_bytes) || overlaps(out, out_bytes, k_pool, pool_bytes) ||
-      overlaps(out, out_bytes, v_pool, pool_bytes))
-    return PKV_ERR_ALIAS;
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, 1,
+                     max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
+                     n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
+                     workspace_bytes, stream);
+}
 
-  const Plan plan = make_plan(num_seqs, n_heads, n_kv_heads, d_head, max_context_len,
-                              partition_tokens);
-  if (!plan.split && plan.parts > 65535) return PKV_ERR_PARTITION;   // grid y limit
-  if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned16(workspace)))
-    return PKV_ERR_WORKSPACE;
+size_t pkv_multi_query_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t n_heads,
+                                       int32_t n_kv_heads, int32_t d_head,
+                                       int32_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs <= 0 || n_heads <= 0 || d_head <= 0 || max_context_len <= 0 ||
+      !valid_group(n_heads, n_kv_heads) || !valid_q_len(q_len, n_heads, n_kv_heads) ||
+      partition_tokens < 0 || partition_tokens % pkv::kBlockTokens)
+    return 0;
+  return make_plan(num_seqs, q_len, n_heads, n_kv_heads, d_head, max_context_len,
+                   partition_tokens).bytes;
+}
 
-  pkv::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_pool = static_cast<const char*>(k_pool);
-  a.v_pool = static_cast<const char*>(v_pool);
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.num_seqs = num_seqs;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.max_context_len = max_context_len;
-  a.n_heads = n_heads;
-  a.n_kv_heads = n_kv_heads;
-  a.split = plan.split ? 1 : 0;
-  a.partition_tokens = plan.partition;
-  a.max_partitions = (int32_t)plan.parts;
-  a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
-  if (plan.bytes > 0) {
-    char* ws = static_cast<char*>(workspace);
-    const size_t pre = align256(plan.prefix_ints * sizeof(int32_t));
-    const size_t vec = align256(plan.records * sizeof(float));
-    a.ws_prefix = plan.prefix_ints ? reinterpret_cast<int32_t*>(ws) : nullptr;
-    a.ws_m = reinterpret_cast<float*>(ws + pre);
-    a.ws_l = reinterpret_cast<float*>(ws + pre + vec);
-    a.ws_o = reinterpret_cast<float*>(ws + pre + 2 * vec);
-  }
-  const hipError_t e = pkv::launch_decode(a, dtype, d_head, n_heads / n_kv_heads, stream);
-  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+int32_t pkv_paged_multi_query_attention(void* out, const void* q, const void* k_pool,
+                                        const void* v_pool, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t q_len, int32_t max_blocks_per_seq,
+                                        int32_t num_blocks, int32_t max_context_len,
+                                        int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+                                        int32_t d_head, float scale, int32_t partition_tokens,
+                                        int32_t dtype, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, q_len,
+                     max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
+                     n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

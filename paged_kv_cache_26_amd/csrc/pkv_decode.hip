@@ -259,28 +259,15 @@ __device__ __forceinline__ void store_row_chunk(void* base, size_t idx, const fl
   }
 }
 
-// One wave: blocks [blk_begin, blk_begin + n_my) of sequence b, KV head j, into st
-// (lane-partial; finish_rows completes it). Tokens >= tok_end are masked. bad is set if a
-// table entry is outside the pool (the data of that block is then not read).
-template <int DT, int D, int G>
-__device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const DecodeArgs& a,
-                                       int b, int j, int blk_begin, int n_my, int tok_end,
-                                       int lane) {
+// Stream blocks [blk_begin, blk_begin + n_my) of sequence b, KV head j through one wave:
+// table entries are preloaded 64 at a time into a VGPR, K/V of the next kDepth blocks are
+// in flight while `process(tile, first_token_of_block)` runs on the current one. bad is set
+// if a table entry is outside the pool (the data of that block is then not read).
+template <int DT, int D, typename F>
+__device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
+                                              int n_my, int lane, int& bad, F&& process) {
   using G_ = Geo<DT, D>;
   const int r = lane >> 4, c = lane & 15;
-  const size_t head_row0 = (size_t)b * a.n_heads + (size_t)j * G;
-
-  // Query fragments (MFMA B operand): head c of this KV group, zero for c >= G.
-  u32x4 qf[G_::kNK];
-  {
-    const char* qrow = static_cast<const char*>(a.q) + (head_row0 + (c < G ? c : 0)) * G_::kRow;
-#pragma unroll
-    for (int kk = 0; kk < G_::kNK; ++kk) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      qf[kk] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 64 * kk + 16 * r) : z;
-    }
-  }
-
   const size_t tok_stride = (size_t)a.n_kv_heads * G_::kRow;        // bytes between tokens
   const size_t blk_stride = tok_stride * kBlockTokens;
   const size_t head_off = (size_t)j * G_::kRow;
@@ -318,9 +305,180 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
         if (((i + kDepth) & 63) == 0) load_table(i + kDepth);
         fetch(tt[(u + kDepth) % NB], i + kDepth);
       }
-      process_block<DT, D, G>(st, tt[u], qf, (blk_begin + i) * kBlockTokens, tok_end,
-                              a.scale_log2, r);
+      process(tt[u], (blk_begin + i) * kBlockTokens);
     }
+  }
+}
+
+// Query fragments (MFMA B operand) for lane column c: 16-byte slices at 64*kk + 16*r of
+// the query row `row` of the output layout, zero when the column is unused.
+template <int DT, int D>
+__device__ __forceinline__ void load_query(const DecodeArgs& a, bool used, size_t row, int r,
+                                           u32x4 (&qf)[Geo<DT, D>::kNK]) {
+  using G_ = Geo<DT, D>;
+  const char* qrow = static_cast<const char*>(a.q) + (used ? row : 0) * G_::kRow;
+#pragma unroll
+  for (int kk = 0; kk < G_::kNK; ++kk) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qf[kk] = used ? *reinterpret_cast<const u32x4*>(qrow + 64 * kk + 16 * r) : z;
+  }
+}
+
+// One wave: blocks [blk_begin, blk_begin + n_my) of sequence b, KV head j, into st
+// (lane-partial; finish_rows completes it). Tokens >= tok_end are masked.
+template <int DT, int D, int G>
+__device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const DecodeArgs& a,
+                                       int b, int j, int blk_begin, int n_my, int tok_end,
+                                       int lane) {
+  const int r = lane >> 4, c = lane & 15;
+  u32x4 qf[Geo<DT, D>::kNK];
+  load_query<DT, D>(a, c < G, (size_t)b * a.n_heads + (size_t)j * G + c, r, qf);
+  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
+    process_block<DT, D, G>(st, t, qf, tok0, tok_end, a.scale_log2, r);
+  });
+}
+
+// ---------------------------------------------------------------------------------------
+// Several new tokens per sequence (q_len = QL > 1): the 16 MFMA columns are the pairs
+// (new query i, head h), column c = i * G + h, C = G * QL <= 16. Query i of sequence b sees
+// tokens 0 .. N_b - QL + i (the causal mask of "09-inference-optimization", KV Cache). With
+// every column in use, P.V also runs on the matrix cores (v_mfma_f32_16x16x4_f32): for load
+// jj, lane (r, c) holds V[token 4r+jj][d = EPL*c + e] — the A operand of instance e — and
+// P[column c][token 4r+jj], its own softmax output — the B operand. No broadcast is needed;
+// the result lands as O[column c][d = EPL*(4r'+i) + e] in accumulator e, element i.
+// ---------------------------------------------------------------------------------------
+
+template <int DT, int D>
+struct MqState {
+  float m = -INFINITY;                          // running max (base 2) of column c
+  float l = 0.f;                                // lane-partial running sum of column c
+  f32x4 o[Geo<DT, D>::kEPL] = {};               // see above
+};
+
+// lim: this lane's column sees tokens < lim; lim_min: the smallest lim of the wave.
+template <int DT, int D>
+__device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<DT, D>& t,
+                                                 const u32x4 (&qf)[Geo<DT, D>::kNK], int blk_tok0,
+                                                 int tok_end, int lim, int lim_min,
+                                                 float scale_log2, int r) {
+  using G_ = Geo<DT, D>;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < G_::kNK; ++kk) {
+    if constexpr (DT == 2) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[kk]),
+                                                    __builtin_bit_cast(bf16x8, qf[kk]), acc, 0, 0, 0);
+    } else if constexpr (DT == 1) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, t.k[kk]),
+                                                   __builtin_bit_cast(f16x8, qf[kk]), acc, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(t.k[kk][s]), as_f(qf[kk][s]), acc, 0, 0, 0);
+    }
+  }
+  const bool partial = blk_tok0 + kBlockTokens > lim_min;
+  const int tok0 = blk_tok0 + 4 * r;
+  float s[4];
+  if (partial) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = (tok0 + i < lim) ? acc[i] * scale_log2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] = acc[i] * scale_log2;
+  }
+  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(st.m, bm);
+  // a column can see none of a block's tokens (its causal limit lies before the block)
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;
+  const float alpha = exp2_fast(st.m - m_use);
+  float p[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) p[i] = exp2_fast(s[i] - m_use);
+  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  st.m = m_new;
+#pragma unroll
+  for (int e = 0; e < G_::kEPL; ++e) st.o[e] *= alpha;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    float v[G_::kEPL];
+    widen<DT, G_::kVW>(t.v[jj], v);
+    if (blk_tok0 + kBlockTokens > tok_end) {
+      const bool valid = tok0 + jj < tok_end;
+#pragma unroll
+      for (int e = 0; e < G_::kEPL; ++e) v[e] = valid ? v[e] : 0.f;   // unused slots may hold NaN
+    }
+#pragma unroll
+    for (int e = 0; e < G_::kEPL; ++e)
+      st.o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[e], p[jj], st.o[e], 0, 0, 0);
+  }
+}
+
+// Output row of column c of KV head j: [b][i][j*G + h] in the [B, q_len, H] row layout.
+template <int G>
+__device__ __forceinline__ size_t mq_row(const DecodeArgs& a, int b, int j, int c) {
+  const int i = c / G, h = c - i * G;
+  return ((size_t)b * a.q_len + i) * a.n_heads + (size_t)j * G + h;
+}
+
+template <int DT, int D, int G>
+__device__ __forceinline__ void attend_mq(MqState<DT, D>& st, int& bad, const DecodeArgs& a,
+                                          int b, int j, int blk_begin, int n_my, int tok_end,
+                                          int n_ctx, int lane) {
+  const int C = G * a.q_len;
+  const int r = lane >> 4, c = lane & 15;
+  u32x4 qf[Geo<DT, D>::kNK];
+  load_query<DT, D>(a, c < C, mq_row<G>(a, b, j, c < C ? c : 0), r, qf);
+  const int first_visible_end = n_ctx - a.q_len + 1;     // limit of query 0
+  const int lim = c < C ? min(tok_end, first_visible_end + c / G) : tok_end;
+  const int lim_min = min(tok_end, first_visible_end);
+  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
+    process_block_mq<DT, D>(st, t, qf, tok0, tok_end, lim, lim_min, a.scale_log2, r);
+  });
+}
+
+template <int DT, int D, int G>
+__device__ __forceinline__ void write_final_mq(const DecodeArgs& a, const MqState<DT, D>& st,
+                                               int bad, int b, int j, int lane) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  if (c >= G * a.q_len) return;
+  const float inv = 1.0f / st.l;
+  const float qnan = __builtin_nanf("");
+  const size_t row = mq_row<G>(a, b, j, c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[G_::kEPL];
+#pragma unroll
+    for (int e = 0; e < G_::kEPL; ++e) v[e] = bad ? qnan : st.o[e][i] * inv;
+    store_row_chunk<DT, G_::kEPL>(a.out, row * D + G_::kEPL * (4 * r + i), v);
+  }
+}
+
+// Record of column c at index rec(c).
+template <int DT, int D, int G, typename R>
+__device__ __forceinline__ void write_record_mq(const DecodeArgs& a, const MqState<DT, D>& st,
+                                                int bad, int lane, R&& rec) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  if (c >= G * a.q_len) return;
+  const float qnan = __builtin_nanf("");
+  const size_t idx = rec(c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float* dst = a.ws_o + idx * D + G_::kEPL * (4 * r + i);
+#pragma unroll
+    for (int e = 0; e < G_::kEPL; e += 4) {
+      const f32x4 x = {bad ? qnan : st.o[e][i], bad ? qnan : st.o[e + 1][i],
+                       bad ? qnan : st.o[e + 2][i], bad ? qnan : st.o[e + 3][i]};
+      *reinterpret_cast<f32x4*>(dst + e) = x;
+    }
+  }
+  if (r == 0) {
+    a.ws_m[idx] = bad ? qnan : st.m;
+    a.ws_l[idx] = bad ? qnan : st.l;
   }
 }
 
@@ -361,17 +519,17 @@ __device__ __forceinline__ void write_final(const DecodeArgs& a, const WaveState
   }
 }
 
-// Partial record of head h at index rec0 + h * rec_stride.
-template <int DT, int D, int G>
+// Partial record of head h at index rec(h).
+template <int DT, int D, int G, typename R>
 __device__ __forceinline__ void write_record(const DecodeArgs& a, const WaveState<DT, D, G>& st,
-                                             int bad, size_t rec0, size_t rec_stride, int lane) {
+                                             int bad, int lane, R&& rec) {
   using G_ = Geo<DT, D>;
   const int r = lane >> 4, c = lane & 15;
   if (r != 0) return;
   const float qnan = __builtin_nanf("");
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    float* dst = a.ws_o + (rec0 + h * rec_stride) * D + c * G_::kEPL;
+    float* dst = a.ws_o + rec(h) * D + c * G_::kEPL;
 #pragma unroll
     for (int e = 0; e < G_::kEPL; e += 4) {
       const f32x4 x = {bad ? qnan : st.o[h][e], bad ? qnan : st.o[h][e + 1],
@@ -380,9 +538,9 @@ __device__ __forceinline__ void write_record(const DecodeArgs& a, const WaveStat
     }
   }
   if (c < G) {
-    const size_t rec = rec0 + c * rec_stride;
-    a.ws_m[rec] = bad ? qnan : st.m;
-    a.ws_l[rec] = bad ? qnan : st.l;
+    const size_t idx = rec(c);
+    a.ws_m[idx] = bad ? qnan : st.m;
+    a.ws_l[idx] = bad ? qnan : st.l;
   }
 }
 
@@ -393,19 +551,51 @@ __device__ __forceinline__ void write_nan_rows(const DecodeArgs& a, size_t row0,
     store_elem<DT>(a.out, row0 * D + i, __builtin_nanf(""));
 }
 
+// A whole-sequence-or-segment of one wave: attend over blocks [blk_begin, +n_my) of
+// sequence b for KV head j, then write the outputs (whole) or the records rec(column).
+template <int DT, int D, int G, bool MQ, typename R>
+__device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, int blk_begin,
+                                            int n_my, int tok_end, int n_ctx, bool whole,
+                                            int lane, R&& rec) {
+  int bad = 0;
+  if constexpr (!MQ) {
+    WaveState<DT, D, G> st;
+    attend<DT, D, G>(st, bad, a, b, j, blk_begin, n_my, tok_end, lane);
+    finish_rows<DT, D, G>(st);
+    if (whole)
+      write_final<DT, D, G>(a, st, bad, (size_t)b * a.n_heads + (size_t)j * G, lane);
+    else
+      write_record<DT, D, G>(a, st, bad, lane, rec);
+  } else {
+    MqState<DT, D> st;
+    attend_mq<DT, D, G>(st, bad, a, b, j, blk_begin, n_my, tok_end, n_ctx, lane);
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    if (whole)
+      write_final_mq<DT, D, G>(a, st, bad, b, j, lane);
+    else
+      write_record_mq<DT, D, G>(a, st, bad, lane, rec);
+  }
+}
+
+__device__ __forceinline__ bool valid_len(const DecodeArgs& a, int n) {
+  return n >= a.q_len && n <= a.max_context_len;
+}
+
 // Fixed partitions: workgroup = NW waves = KV heads hg*NW .. hg*NW+NW-1 of one
 // (partition, sequence); grid (head groups, partitions, sequences).
-template <int DT, int D, int G, int NW>
+template <int DT, int D, int G, int NW, bool MQ>
 __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
   const int hg = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int j = hg * NW + wave;                 // this wave's KV head
   if (j >= a.n_kv_heads) return;                // no barrier below: waves are independent
-  const size_t head_row0 = (size_t)b * a.n_heads + (size_t)j * G;
+  const int C = G * a.q_len;                    // output rows of this wave
 
   const int n_ctx = a.context_lens[b];
-  if (n_ctx < 1 || n_ctx > a.max_context_len) {
-    if (p == 0) write_nan_rows<DT, D>(a, head_row0, G, lane, 64);
+  if (!valid_len(a, n_ctx)) {
+    if (p == 0)
+      for (int c = 0; c < C; ++c) write_nan_rows<DT, D>(a, mq_row<G>(a, b, j, c), 1, lane, 64);
     return;
   }
   const int P = a.partition_tokens;
@@ -414,15 +604,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
   const int tok_end = min(n_ctx, (p + 1) * P);
   const int blk_begin = (p * P) >> 4;
   const int n_my = ((tok_end + 15) >> 4) - blk_begin;     // >= 1
-
-  WaveState<DT, D, G> st;
-  int bad = 0;
-  attend<DT, D, G>(st, bad, a, b, j, blk_begin, n_my, tok_end, lane);
-  finish_rows<DT, D, G>(st);
-  if (n_part == 1)
-    write_final<DT, D, G>(a, st, bad, head_row0, lane);
-  else
-    write_record<DT, D, G>(a, st, bad, head_row0 * a.max_partitions + p, a.max_partitions, lane);
+  run_segment<DT, D, G, MQ>(a, b, j, blk_begin, n_my, tok_end, n_ctx, n_part == 1, lane,
+                            [&](int c) { return mq_row<G>(a, b, j, c) * a.max_partitions + p; });
 }
 
 // Balanced split: the work is the list of units (head group hg, sequence b, block k) in
@@ -432,8 +615,8 @@ __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
 // segment; a segment holding a whole sequence is finished in place, any other one leaves
 // a record for merge_kernel. Segments of stream s = hg * num_seqs + b are produced by
 // consecutive workgroups in increasing order of w, so (w + s) names each segment
-// uniquely: its G records start at ((w + s) * NW + wave) * G.
-template <int DT, int D, int G, int NW>
+// uniquely: the record of its column c (of C = G * q_len) is ((w + s) * NW + wave) * C + c.
+template <int DT, int D, int G, int NW, bool MQ>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW;
   __shared__ int sm_pref[kSplitMaxSeqs + 1];   // blocks of sequences before b
@@ -448,7 +631,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   for (int s = s0; s < s1; ++s) {
     const int n = a.context_lens[s];
     sm_pref[s] = run;
-    run += (n >= 1 && n <= a.max_context_len) ? (n + kBlockTokens - 1) / kBlockTokens : 0;
+    run += valid_len(a, n) ? (n + kBlockTokens - 1) / kBlockTokens : 0;
   }
   sm_scan[tid] = run;
   __syncthreads();
@@ -471,12 +654,12 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   const long long W = min((long long)gridDim.x, (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
   if (w == 0)
     for (int s = tid; s <= B; s += kThreads) a.ws_prefix[s] = sm_pref[s];
-  for (int s = w; s < B; s += gridDim.x) {      // invalid lengths: NaN outputs
-    const int n = a.context_lens[s];
-    if (n < 1 || n > a.max_context_len)
-      write_nan_rows<DT, D>(a, (size_t)s * a.n_heads, a.n_heads, tid, kThreads);
-  }
+  const int rows_per_seq = a.q_len * a.n_heads;
+  for (int s = w; s < B; s += gridDim.x)        // invalid lengths: NaN outputs
+    if (!valid_len(a, a.context_lens[s]))
+      write_nan_rows<DT, D>(a, (size_t)s * rows_per_seq, rows_per_seq, tid, kThreads);
   if (w >= W) return;
+  const int C = G * a.q_len;
   const long long u1 = (w + 1) * T / W;
   long long u = w * T / W;
   while (u < u1) {
@@ -494,40 +677,38 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
     const int n_my = (int)(seg_end - u);
     const int j = hg * NW + wave;
     if (j < a.n_kv_heads) {
-      const int tok_end = min(a.context_lens[b], (blk0 + n_my) * kBlockTokens);
-      WaveState<DT, D, G> st;
-      int bad = 0;
-      attend<DT, D, G>(st, bad, a, b, j, blk0, n_my, tok_end, lane);
-      finish_rows<DT, D, G>(st);
-      const size_t head_row0 = (size_t)b * a.n_heads + (size_t)j * G;
-      if (blk0 == 0 && n_my == nb) {
-        write_final<DT, D, G>(a, st, bad, head_row0, lane);
-      } else {
-        const long long stream = (long long)hg * B + b;
-        write_record<DT, D, G>(a, st, bad, ((size_t)(w + stream) * NW + wave) * G, 1, lane);
-      }
+      const int n_ctx = a.context_lens[b];
+      const int tok_end = min(n_ctx, (blk0 + n_my) * kBlockTokens);
+      const size_t rec0 = ((size_t)(w + (long long)hg * B + b) * NW + wave) * C;
+      run_segment<DT, D, G, MQ>(a, b, j, blk0, n_my, tok_end, n_ctx, blk0 == 0 && n_my == nb,
+                                lane, [&](int c) { return rec0 + c; });
     }
     u = seg_end;
   }
 }
 
-// One workgroup per (sequence, query head): combine that head's records by the rescale
-// rule. Fixed mode: the head's partitions. Split mode: the segments of its stream.
+// One workgroup per output row (sequence b, new query i, head h): combine that row's
+// records by the rescale rule. Fixed mode: the partitions. Split mode: the segments of its
+// stream.
 template <int DT, int D, int NW>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int Q4 = D / 4;          // float4 chunks per output row
   constexpr int PR = 256 / Q4;       // records read side by side
-  const int bh = blockIdx.x;
-  const int b = bh / a.n_heads, h = bh - b * a.n_heads;
+  const int row = blockIdx.x;        // (b * q_len + i) * n_heads + h
+  const int per_seq = a.q_len * a.n_heads;
+  const int b = row / per_seq;
+  const int i = (row - b * per_seq) / a.n_heads;
+  const int h = row - b * per_seq - i * a.n_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_ctx = a.context_lens[b];
-  if (n_ctx < 1 || n_ctx > a.max_context_len) return;     // decode wrote NaN
+  if (!valid_len(a, n_ctx)) return;                      // decode wrote NaN
 
   size_t base, stride;
   int n_rec;
   if (a.split) {
     const int B = a.num_seqs;
     const int G = a.n_heads / a.n_kv_heads;
+    const int C = G * a.q_len;
     const int j = h / G, hh = h - j * G;
     const int hg = j / NW, wv = j - hg * NW;
     const int HG = (a.n_kv_heads + NW - 1) / NW;
@@ -541,12 +722,12 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     const long long last = ((U + nb) * W - 1) / T;
     if (first == last) return;                              // decode wrote the output
     n_rec = (int)(last - first + 1);
-    base = ((size_t)(first + (long long)hg * B + b) * NW + wv) * G + hh;
-    stride = (size_t)NW * G;
+    base = ((size_t)(first + (long long)hg * B + b) * NW + wv) * C + (size_t)i * G + hh;
+    stride = (size_t)NW * C;
   } else {
     n_rec = (n_ctx + a.partition_tokens - 1) / a.partition_tokens;
     if (n_rec <= 1) return;                                 // decode wrote the output
-    base = (size_t)bh * a.max_partitions;
+    base = (size_t)row * a.max_partitions;
     stride = 1;
   }
 
@@ -589,7 +770,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     for (int k = 1; k < PR; ++k) t += part[k][tid];
     const float inv = 1.0f / L;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) store_elem<DT>(a.out, (size_t)bh * D + 4 * tid + x, t[x] * inv);
+    for (int x = 0; x < 4; ++x) store_elem<DT>(a.out, (size_t)row * D + 4 * tid + x, t[x] * inv);
   }
 }
 
@@ -609,23 +790,30 @@ int resident_workgroups(K kernel, int threads) {
   return per_cu * cus;
 }
 
-template <int DT, int D, int G, int NW>
+template <int DT, int D, int G, int NW, bool MQ>
 hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
   bool need_merge;
   if (a.split) {
-    auto kernel = decode_split_kernel<DT, D, G, NW>;
+    auto kernel = decode_split_kernel<DT, D, G, NW, MQ>;
     a.split_workgroups = min(kSplitMaxWorkgroups, resident_workgroups(kernel, 64 * NW));
     hipLaunchKernelGGL(kernel, dim3(a.split_workgroups), dim3(64 * NW), 0, stream, a);
     need_merge = true;
   } else {
     const dim3 grid((a.n_kv_heads + NW - 1) / NW, a.max_partitions, a.num_seqs);
-    hipLaunchKernelGGL((decode_fixed_kernel<DT, D, G, NW>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((decode_fixed_kernel<DT, D, G, NW, MQ>), grid, dim3(64 * NW), 0, stream, a);
     need_merge = a.max_partitions > 1;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !need_merge) return e;
-  hipLaunchKernelGGL((merge_kernel<DT, D, NW>), dim3(a.num_seqs * a.n_heads), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((merge_kernel<DT, D, NW>), dim3(a.num_seqs * a.q_len * a.n_heads), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+template <int DT, int D, int G, int NW>
+hipError_t launch_mq(const DecodeArgs& a, hipStream_t stream) {
+  if (a.q_len == 1) return launch_typed<DT, D, G, NW, false>(a, stream);
+  return launch_typed<DT, D, G, NW, true>(a, stream);
 }
 
 template <int DT, int D, int G>
@@ -633,9 +821,9 @@ hipError_t launch_waves(const DecodeArgs& a, hipStream_t stream) {
   // Eight KV heads per workgroup when they divide evenly and the kernel fits 256 registers
   // per lane (16-bit types, G <= 4); otherwise four (waves past the last head exit).
   if constexpr (DT != 0 && G <= 4) {
-    if (max_waves_per_workgroup(a.n_kv_heads) == 8) return launch_typed<DT, D, G, 8>(a, stream);
+    if (max_waves_per_workgroup(a.n_kv_heads) == 8) return launch_mq<DT, D, G, 8>(a, stream);
   }
-  return launch_typed<DT, D, G, 4>(a, stream);
+  return launch_mq<DT, D, G, 4>(a, stream);
 }
 
 template <int DT, int D>

@@ -24,8 +24,8 @@ struct AppendArgs {
   const char* k_new;
   const char* v_new;
   const int32_t* block_tables;
-  const int32_t* positions;
-  int32_t num_seqs, max_blocks_per_seq, num_blocks;
+  const int32_t* positions;          // first new token of each sequence
+  int32_t num_seqs, n_tokens, max_blocks_per_seq, num_blocks;
   int32_t row_bytes;                 // n_kv_heads * d_head * element bytes
 };
 
@@ -55,6 +55,7 @@ struct DecodeArgs {
   int32_t* ws_prefix;                // split mode: [num_seqs + 1] block prefix sums
   int32_t num_seqs, max_blocks_per_seq, num_blocks, max_context_len;
   int32_t n_heads, n_kv_heads;
+  int32_t q_len;                     // new tokens (queries) per sequence, 1..16/group
   int32_t split;                     // 1: balanced split over the GPU; 0: fixed partitions
   int32_t partition_tokens, max_partitions;   // fixed mode
   int32_t split_workgroups;          // split mode: grid size W (set by the launcher)

@@ -36,6 +36,15 @@ _SIGNATURES = {
     "pkv_gather_kv": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_ptr]),
     "pkv_status_str": (ctypes.c_char_p, [_c_i32]),
+    "pkv_kv_append_tokens": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32,
+                                      _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                      _c_ptr]),
+    "pkv_paged_multi_query_attention": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr,
+                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_i32,
+                                                 _c_i32, _c_ptr, _c_size, _c_ptr]),
+    "pkv_multi_query_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                  _c_i32]),
     # block manager (include/pkv_block_manager.h)
     "pkv_bm_create": (_c_ptr, [_c_i32, _c_i32, _c_ptr]),
     "pkv_bm_destroy": (None, [_c_ptr]),
@@ -171,6 +180,58 @@ def pkv_paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_len
         _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_paged_decode_attention")
+    return out
+
+
+def pkv_kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, positions,
+                         stream=None) -> None:
+    """Write k_new/v_new [B, n_tokens, H_kv, d] at positions[b] + i (in place)."""
+    lib = load_library()
+    _check_device(k_pool, v_pool, k_new, v_new, block_tables, positions)
+    _require(k_pool.dtype in _DTYPE_CODE, "unsupported dtype")
+    _require(k_new.shape == v_new.shape and k_new.dim() == 4,
+             "k_new/v_new must be [B, n_tokens, H_kv, d]")
+    B, n = k_new.shape[0], k_new.shape[1]
+    st = lib.pkv_kv_append_tokens(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+                                  _ptr(block_tables), _ptr(positions), B, n,
+                                  block_tables.shape[1], k_pool.shape[0], k_pool.shape[1],
+                                  k_pool.shape[2], k_pool.shape[3], _DTYPE_CODE[k_pool.dtype],
+                                  _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_kv_append_tokens")
+
+
+def pkv_multi_query_workspace_bytes(num_seqs: int, q_len: int, n_heads: int, n_kv_heads: int,
+                                    d_head: int, max_context_len: int,
+                                    partition_tokens: int = 0) -> int:
+    return int(load_library().pkv_multi_query_workspace_bytes(
+        num_seqs, q_len, n_heads, n_kv_heads, d_head, max_context_len, partition_tokens))
+
+
+def pkv_paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, context_lens,
+                                    max_context_len: int, scale: float | None = None,
+                                    partition_tokens: int = 0, workspace=None, stream=None):
+    """q/out [B, q_len, H, d]; new query i of sequence b sees tokens < N_b - q_len + i + 1."""
+    lib = load_library()
+    _check_device(out, q, k_pool, v_pool, block_tables, context_lens)
+    _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype,
+             "q, out and pools must share a supported dtype")
+    _require(q.dim() == 4 and out.shape == q.shape, "q/out must be [B, q_len, H, d]")
+    B, ql, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = pkv_multi_query_workspace_bytes(B, ql, H, k_pool.shape[2], d, max_context_len,
+                                           partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pkv_paged_multi_query_attention(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+        B, ql, block_tables.shape[1], k_pool.shape[0], int(max_context_len), k_pool.shape[1], H,
+        k_pool.shape[2], d, float(scale), int(partition_tokens), _DTYPE_CODE[q.dtype],
+        _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_paged_multi_query_attention")
     return out
 
 

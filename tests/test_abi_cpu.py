@@ -79,7 +79,7 @@ def test_workspace_bytes(lib):
 
 def test_status_strings(lib):
     assert pkv.pkv_status_str(0) == "ok"
-    for code in range(-16, 0):
+    for code in range(-17, 0):
         s = pkv.pkv_status_str(code)
         assert s and s != "unknown status"
     assert pkv.pkv_status_str(5) == "unknown status"
@@ -112,6 +112,29 @@ def _decode_call(lib, **over):
 ])
 def test_decode_rejects_bad_arguments_on_host(lib, over, code):
     assert _decode_call(lib, **over) == code
+
+
+def test_multi_query_rejects_bad_arguments_on_host(lib):
+    f = lib.pkv_paged_multi_query_attention
+    args = dict(out=0x1000000, q=0x2000000, k=0x10000000, v=0x20000000, tab=0x30000,
+                lens=0x40000, B=4, ql=4, mbps=64, nblk=64, maxctx=700, bs=16, H=32, Hkv=8, d=128, scale=0.1, P=0,
+                dtype=2, ws=0, wsb=0)
+
+    def call(**over):
+        a = dict(args, **over)
+        return f(a["out"], a["q"], a["k"], a["v"], a["tab"], a["lens"], a["B"], a["ql"],
+                 a["mbps"], a["nblk"], a["maxctx"], a["bs"], a["H"], a["Hkv"], a["d"],
+                 a["scale"], a["P"], a["dtype"], a["ws"], a["wsb"], None)
+    assert call(ql=5) == -17                 # 5 queries x 4 heads per KV head > 16
+    assert call(ql=0) == -17
+    assert call(maxctx=3) == -7              # fewer tokens than new queries
+    assert call() == -9                      # needs a workspace
+    ws = pkv.pkv_multi_query_workspace_bytes
+    assert ws(4, 4, 32, 8, 128, 700, 0) > ws(4, 1, 32, 8, 128, 700, 0) > 0
+    assert ws(4, 5, 32, 8, 128, 700, 0) == 0
+    g = lib.pkv_kv_append_tokens
+    assert g(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 4, 17, 8, 64, 16, 4, 64, 0, None) == -2
+    assert g(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 0x6000, 4, 0, 8, 64, 16, 4, 64, 0, None) == -2
 
 
 def test_append_and_gather_reject_bad_arguments_on_host(lib):
