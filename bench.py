@@ -65,11 +65,14 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a buffer of this many MiB 3 times (a dispatch of "
                          "known traffic for scaling hardware byte counters)")
-    ap.add_argument("--component", choices=["decode", "block-manager", "multi-query"],
+    ap.add_argument("--component",
+                    choices=["decode", "block-manager", "multi-query", "shared-prefix"],
                     default="decode",
                     help="decode: the decode step (default); block-manager: the native block "
                          "manager and the copy-on-write block copy; multi-query: q_len new "
-                         "tokens per sequence (speculative verification) on the GQA workload")
+                         "tokens per sequence (speculative verification) on the GQA workload; "
+                         "shared-prefix: the shared-prefix workload with each group's common "
+                         "blocks read once")
     ap.add_argument("--q-len", type=int, default=4, help="new tokens per sequence (multi-query)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
@@ -444,6 +447,89 @@ def run_multi_query(args) -> dict:
     }
 
 
+def run_shared_prefix(args) -> dict:
+    """The shared-prefix workload (bf16, 128 sequences in 8 groups of 16 over a 2048-token
+    prefix, suffixes U{64..1024}, 32 query / 8 KV heads, d 128): one step appends every new
+    token and runs pkv_paged_decode_attention_shared_prefix, which reads each group's 128
+    shared blocks once. Compared with pkv_paged_decode_attention on the same batch, which
+    reads them once per sequence."""
+    import torch
+
+    from paged_kv_cache_26_amd import pkv
+    from paged_kv_cache_26_amd import workload as wlm
+    from paged_kv_cache_26_amd.block_manager import find_shared_prefixes
+
+    pkv.load_library()
+    wl = wlm.make_workload(5)
+    spec = wl.spec
+    dev = torch.device("cuda:0")
+    t = wlm.to_torch(wl, dev)
+    out = torch.empty_like(t["q"])
+    t_host = time.perf_counter()
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    group_us = (time.perf_counter() - t_host) * 1e6
+    sg = torch.from_numpy(grp.seq_group).to(dev)
+    gb = torch.from_numpy(grp.group_blocks).to(dev)
+    need = pkv.pkv_shared_prefix_workspace_bytes(wl.batch, spec.n_heads, spec.n_kv_heads,
+                                                 spec.d_head, grp.max_shared_blocks)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    need1 = pkv.pkv_decode_workspace_bytes(wl.batch, spec.n_heads, spec.n_kv_heads, spec.d_head,
+                                           wl.max_context_len, 0)
+    ws1 = torch.empty(max(need1, 1), dtype=torch.uint8, device=dev)
+
+    def append():
+        pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                          t["positions"])
+
+    def shared():
+        pkv.pkv_paged_decode_attention_shared_prefix(
+            out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"], t["context_lens"], sg, gb,
+            grp.max_group_size, grp.max_shared_blocks, wl.max_context_len, wl.scale, ws)
+
+    def plain():
+        pkv.pkv_paged_decode_attention(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                                       t["context_lens"], wl.max_context_len, wl.scale, 0, ws1)
+
+    def step():
+        append()
+        shared()
+
+    s_step = _time_launches(step, args.steps, args.warmup)
+    s_shared = _time_launches(shared, args.steps, args.warmup)
+    s_plain = _time_launches(plain, args.steps, args.warmup)
+    by = algorithmic_bytes(wl)
+    q_out = 2 * wl.q.nbytes
+    tables = int(sum(-(-int(n) // 16) for n in wl.context_lens)) * 4
+    alg = by["kv_unique"] + q_out + tables
+    gbps = alg / s_shared / 1e9
+    return {
+        "metric": "shared-prefix paged decode: logical KV GB/s (tokens attended x bytes); us/step",
+        "value": round(by["kv"] / s_step / 1e9, 2),
+        "unit": "GB/s",
+        "higher_is_better": True,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "dtype": spec.dtype,
+        "data": "synthetic (seeded)",
+        "us_per_step": round(s_step * 1e6, 2),
+        "config": {"workload": spec.name, "batch": spec.batch, "groups": spec.groups,
+                   "prefix_len": spec.prefix_len, "suffix_range": list(spec.suffix_range),
+                   "n_heads": spec.n_heads, "n_kv_heads": spec.n_kv_heads,
+                   "d_head": spec.d_head, "context_tokens": int(wl.context_lens.sum()),
+                   "kv_bytes_per_step": by["kv"], "kv_unique_bytes_per_step": by["kv_unique"]},
+        "attention_us": round(s_shared * 1e6, 2),
+        "plain_decode_attention_us": round(s_plain * 1e6, 2),
+        "speedup_vs_plain_decode": round(s_plain / s_shared, 2),
+        "unique_kv_gbps": round(by["kv_unique"] / s_shared / 1e9, 1),
+        "host_grouping_us": round(group_us, 1),
+        "roofline": {"bound": "hbm", "kernel": "shared-prefix decode launch (prefix pass, split "
+                     "pass, merge)", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -457,6 +543,9 @@ def main():
         return
     if args.component == "multi-query":
         print(json.dumps(run_multi_query(args)), flush=True)
+        return
+    if args.component == "shared-prefix":
+        print(json.dumps(run_shared_prefix(args)), flush=True)
         return
     cfgs = [1, 2, 3, 4, 5] if args.all else [args.config]
     for cfg in cfgs:

@@ -28,9 +28,12 @@
  *     never synchronises: each call checks its arguments on the host, enqueues its
  *     kernels on `stream` and returns.
  *   * dtype is one of PKV_F32, PKV_F16, PKV_BF16; K, V, q, k_new, v_new and out share it.
- *     Arithmetic is fp32 throughout (fp32 products and accumulation); outputs are
- *     rounded to the dtype with round-to-nearest-even.
- *   * Supported shapes: block_size == 16, d_head in {64, 128},
+ *     Arithmetic is fp32 (fp32 products and accumulation), with one exception: where
+ *     the weighted sum of V runs on the matrix cores for 16 query columns at once
+ *     (multi-query attention and the shared-prefix pass, 16-bit dtypes), the softmax
+ *     weights are rounded to the dtype first, and the running sum uses the same
+ *     rounded weights. Outputs are rounded to the dtype with round-to-nearest-even.
+ *   * Supported shapes: block_size == 16, d_head in {64, 128}, 1 <= n_kv_heads <= 256,
  *     n_heads / n_kv_heads in {1, 2, 4, 8}. All device pointers must be 16-byte aligned.
  *   * Return value: PKV_OK (0) or a negative PKV_ERR_* code. Errors are found on the
  *     host before anything is enqueued (except PKV_ERR_LAUNCH). Device-side values
@@ -205,6 +208,49 @@ int32_t pkv_paged_multi_query_attention(void* out, const void* q, const void* k_
 size_t pkv_multi_query_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t n_heads,
                                        int32_t n_kv_heads, int32_t d_head,
                                        int32_t max_context_len, int32_t partition_tokens);
+
+/*
+ * pkv_paged_decode_attention_shared_prefix - pkv_paged_decode_attention for a batch in
+ * which groups of sequences share the first blocks of their tables (a common prompt,
+ * parallel sampling, beam search), reading every shared block once per group.
+ *
+ * Source: "LLM推理与服务：面试问题与推荐回答" Q2 and Q3 (sequences share physical blocks of a
+ * common prefix, stored once); "Scaling Book 第 11 章" §11.3-§11.4 (prefix caching).
+ * The attention computed is exactly that of pkv_paged_decode_attention; the grouping only
+ * changes how the shared blocks are read: a prefix pass streams each group's shared blocks
+ * once and scores them against the queries of all members (up to 64 (member, head)
+ * columns per KV head per workgroup), then the balanced split covers each sequence's own
+ * blocks, and the merge kernel combines the two.
+ *
+ *   seq_group        [num_seqs] int32 device: group of each sequence in [0, n_groups), or
+ *                    -1 for none.
+ *   group_blocks     [n_groups] int32 device: number of leading table entries every member
+ *                    of the group shares (whole blocks; 0 = nothing shared). The shared
+ *                    blocks are read through the table of the group's first member (lowest
+ *                    sequence index). NaN outputs mark broken promises: a member whose
+ *                    table differs from the first member's inside the shared run, or whose
+ *                    context ends inside it (the new token is never in a shared block);
+ *                    every member of a group that shares blocks and has more than
+ *                    max_group_size members, or more than max_shared_blocks (or
+ *                    max_blocks_per_seq) shared blocks.
+ *   max_group_size   host bound on members per group (sizes the prefix-pass grid).
+ *   max_shared_blocks host bound on group_blocks (sizes the prefix records).
+ * Other arguments as pkv_paged_decode_attention (balanced split, num_seqs <= 4096);
+ * workspace size from pkv_shared_prefix_workspace_bytes.
+ */
+int32_t pkv_paged_decode_attention_shared_prefix(
+    void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_group,
+    const int32_t* group_blocks, int32_t n_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+    int32_t d_head, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
+/* Scratch bytes of pkv_paged_decode_attention_shared_prefix (host only); 0 for invalid
+ * sizes. */
+size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads,
+                                         int32_t d_head, int32_t max_shared_blocks);
 
 /*
  * pkv_kv_bytes_per_token - bytes one token occupies in the KV cache of a whole model:

@@ -93,6 +93,22 @@ int32_t pkv_bm_num_blocks_of(const pkv_block_manager* bm, int64_t seq_id);
 int32_t pkv_bm_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int32_t n,
                       int32_t max_blocks, int32_t* out);
 
+/* Host: group the sequences of a batch by the leading blocks their tables share, for
+ * pkv_paged_decode_attention_shared_prefix. Source: "LLM推理与服务：面试问题与推荐回答"
+ * Q2/Q3 (sequences with a common prefix hold the same physical blocks). tables: HOST int32
+ * [num_seqs][max_blocks]; context_lens: HOST int32 [num_seqs]. Sequences whose first table
+ * entry is the same block form a candidate set (in order of first appearance); a set of at
+ * least min_members (>= 2) sequences becomes a group whose shared block count is the
+ * longest run of leading entries equal in every member's table, cut so that each member
+ * keeps its last token outside it; a set sharing no whole block forms no group.
+ * Outputs: seq_group[num_seqs] (group id or -1), group_blocks[0 .. *n_groups) (caller
+ * provides num_seqs entries), *n_groups, *max_group_size, *max_shared_blocks. */
+int32_t pkv_find_shared_prefixes(const int32_t* tables, int32_t num_seqs, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t block_size,
+                                 int32_t min_members, int32_t* seq_group, int32_t* group_blocks,
+                                 int32_t* n_groups, int32_t* max_group_size,
+                                 int32_t* max_shared_blocks);
+
 /* GPU: copy whole blocks in both pools, pool[dst] = pool[src] for every pair.
  * pairs: DEVICE int32 [n_pairs][2] (src, dst); pools as in pkv.h. Destinations must be
  * distinct and no destination may be a source of another pair. Pairs with an id outside

@@ -108,3 +108,41 @@ class NativeBlockManager:
                                             len(ids), int(max_blocks),
                                             out.ctypes.data_as(ctypes.c_void_p)), "tables")
         return out
+
+
+class SharedPrefixes:
+    """Groups of a batch for pkv_paged_decode_attention_shared_prefix."""
+
+    def __init__(self, seq_group, group_blocks, max_group_size, max_shared_blocks):
+        self.seq_group = seq_group            # [B] int32, group id or -1
+        self.group_blocks = group_blocks      # [n_groups] int32, shared leading blocks
+        self.max_group_size = max_group_size
+        self.max_shared_blocks = max_shared_blocks
+
+    @property
+    def n_groups(self) -> int:
+        return int(self.group_blocks.shape[0])
+
+
+def find_shared_prefixes(tables, context_lens, block_size: int = 16,
+                         min_members: int = 2) -> SharedPrefixes:
+    """Group sequences by the leading physical blocks their tables share (native host code,
+    pkv_find_shared_prefixes)."""
+    lib = pkv.load_library()
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    n = np.ascontiguousarray(context_lens, dtype=np.int32)
+    B = t.shape[0]
+    if t.ndim != 2 or n.shape != (B,):
+        raise ValueError("tables must be [B, max_blocks] and context_lens [B]")
+    seq_group = np.empty(B, np.int32)
+    group_blocks = np.empty(max(B, 1), np.int32)
+    out = [ctypes.c_int32(0) for _ in range(3)]
+    vp = ctypes.c_void_p
+    st = lib.pkv_find_shared_prefixes(t.ctypes.data_as(vp), B, t.shape[1], n.ctypes.data_as(vp),
+                                      int(block_size), int(min_members),
+                                      seq_group.ctypes.data_as(vp), group_blocks.ctypes.data_as(vp),
+                                      *[ctypes.byref(o) for o in out])
+    if st != 0:
+        raise pkv.PkvError(st, "pkv_find_shared_prefixes")
+    ng, mg, ms = (o.value for o in out)
+    return SharedPrefixes(seq_group, group_blocks[:ng].copy(), mg, ms)

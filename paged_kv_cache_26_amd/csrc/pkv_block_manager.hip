@@ -195,6 +195,54 @@ int32_t pkv_bm_tables(const pkv_block_manager* bm, const int64_t* seq_ids, int32
   return PKV_OK;
 }
 
+int32_t pkv_find_shared_prefixes(const int32_t* tables, int32_t num_seqs, int32_t max_blocks,
+                                 const int32_t* context_lens, int32_t block_size,
+                                 int32_t min_members, int32_t* seq_group, int32_t* group_blocks,
+                                 int32_t* n_groups, int32_t* max_group_size,
+                                 int32_t* max_shared_blocks) {
+  if (!n_groups || !max_group_size || !max_shared_blocks) return PKV_ERR_NULL;
+  if (num_seqs > 0 && (!tables || !context_lens || !seq_group || !group_blocks))
+    return PKV_ERR_NULL;
+  if (num_seqs < 0 || max_blocks < 0 || block_size <= 0 || min_members < 2) return PKV_ERR_SHAPE;
+  *n_groups = 0;
+  *max_group_size = 0;
+  *max_shared_blocks = 0;
+  // candidates: sequences with at least one whole block before their last token, keyed by
+  // their first physical block, in order of first appearance
+  std::unordered_map<int32_t, int32_t> slot_of;
+  std::vector<std::vector<int32_t>> sets;
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    seq_group[b] = -1;
+    const int32_t n = context_lens[b];
+    if (n <= block_size || max_blocks == 0) continue;
+    const int32_t first = tables[(size_t)b * max_blocks];
+    if (first < 0) continue;
+    auto ins = slot_of.emplace(first, (int32_t)sets.size());
+    if (ins.second) sets.emplace_back();
+    sets[ins.first->second].push_back(b);
+  }
+  for (const std::vector<int32_t>& m : sets) {
+    if ((int32_t)m.size() < min_members) continue;
+    const int32_t* lead = tables + (size_t)m[0] * max_blocks;
+    int32_t sb = max_blocks;
+    for (int32_t b : m) {
+      const int32_t* row = tables + (size_t)b * max_blocks;
+      int32_t k = 0;
+      const int32_t own = (context_lens[b] - 1) / block_size;   // blocks before the last token
+      const int32_t lim = own < sb ? own : sb;
+      while (k < lim && row[k] == lead[k] && row[k] >= 0) ++k;
+      sb = k;
+    }
+    if (sb == 0) continue;
+    const int32_t g = (*n_groups)++;
+    group_blocks[g] = sb;
+    for (int32_t b : m) seq_group[b] = g;
+    if ((int32_t)m.size() > *max_group_size) *max_group_size = (int32_t)m.size();
+    if (sb > *max_shared_blocks) *max_shared_blocks = sb;
+  }
+  return PKV_OK;
+}
+
 }  // extern "C"
 
 namespace {
@@ -225,7 +273,9 @@ extern "C" int32_t pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pa
   if (eb == 0) return PKV_ERR_DTYPE;
   if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
   if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
-  if (n_pairs < 0 || n_pairs > 65535 || num_blocks <= 0 || n_kv_heads <= 0) return PKV_ERR_SHAPE;
+  if (n_pairs < 0 || n_pairs > 65535 || num_blocks <= 0 || n_kv_heads <= 0 ||
+      n_kv_heads > pkv::kMaxKvHeads)
+    return PKV_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15u)
     return PKV_ERR_ALIGN;
   if (n_pairs == 0) return PKV_OK;

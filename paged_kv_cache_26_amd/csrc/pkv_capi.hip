@@ -4,6 +4,7 @@
 #include "../../include/pkv.h"
 #include "../../include/pkv_block_manager.h"
 
+#include <algorithm>
 #include <cmath>
 
 #include "pkv_internal.h"
@@ -36,12 +37,35 @@ struct Plan {
   int64_t parts;         // fixed mode: partitions of the longest sequence
   size_t records;        // partial-result records the workspace must hold
   size_t prefix_ints;    // split mode: block prefix sums
+  size_t shared_records; // shared-prefix pass records
+  int32_t prefix_parts;  // shared-prefix pass partitions
+  size_t flag_ints;      // shared-prefix member flags
   size_t bytes;          // total workspace bytes
 };
 
 Plan make_plan(int32_t num_seqs, int32_t q_len, int32_t n_heads, int32_t n_kv_heads,
-               int32_t d_head, int32_t max_context_len, int32_t partition_tokens) {
+               int32_t d_head, int32_t max_context_len, int32_t partition_tokens,
+               int32_t max_shared_blocks = -1) {
   Plan p{};
+  if (max_shared_blocks >= 0) {          // shared-prefix decode: always the balanced split
+    const int64_t nw = pkv::max_waves_per_workgroup(n_kv_heads);
+    const int64_t hg = (n_kv_heads + nw - 1) / nw;
+    const int64_t g = n_heads / n_kv_heads;
+    p.split = true;
+    p.records = (size_t)((pkv::kSplitMaxWorkgroups + hg * num_seqs) * nw * g);
+    p.prefix_ints = (size_t)num_seqs + 1;
+    p.prefix_parts = (int32_t)std::max<int64_t>(
+        1, ((int64_t)max_shared_blocks * pkv::kBlockTokens + pkv::kPrefixPartition - 1) /
+               pkv::kPrefixPartition);
+    p.shared_records = (size_t)num_seqs * n_heads * p.prefix_parts;
+    p.flag_ints = (size_t)num_seqs * p.prefix_parts;
+    p.bytes = align256(p.prefix_ints * sizeof(int32_t)) + 2 * align256(p.records * sizeof(float)) +
+              align256(p.records * d_head * sizeof(float)) +
+              2 * align256(p.shared_records * sizeof(float)) +
+              align256(p.shared_records * d_head * sizeof(float)) +
+              align256(p.flag_ints * sizeof(int32_t));
+    return p;
+  }
   // 0 selects the balanced split, except when every sequence fits one 512-token partition
   // (one kernel, no merge) or there are more sequences than the split mode holds.
   p.split = partition_tokens == 0 && num_seqs <= pkv::kSplitMaxSeqs &&
@@ -76,7 +100,8 @@ int32_t check_pool_args(int32_t num_seqs, int32_t max_blocks_per_seq, int32_t nu
   if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
   if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
   if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
-  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || n_kv_heads <= 0)
+  if (num_seqs <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 || n_kv_heads <= 0 ||
+      n_kv_heads > pkv::kMaxKvHeads)
     return PKV_ERR_SHAPE;
   if (num_seqs > 65535) return PKV_ERR_SHAPE;   // grid z / y limit
   if (max_context_len < 1 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
@@ -205,7 +230,7 @@ int32_t pkv_kv_append_tokens(void* k_pool, void* v_pool, const void* k_new, cons
   if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
   if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
   if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
-      n_kv_heads <= 0 || n_tokens < 1 || n_tokens > 16)
+      n_kv_heads <= 0 || n_kv_heads > pkv::kMaxKvHeads || n_tokens < 1 || n_tokens > 16)
     return PKV_ERR_SHAPE;
   if (!aligned16(k_pool) || !aligned16(v_pool) || !aligned16(k_new) || !aligned16(v_new))
     return PKV_ERR_ALIGN;
@@ -300,6 +325,86 @@ int32_t pkv_paged_multi_query_attention(void* out, const void* q, const void* k_
                      max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
                      n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
                      workspace_bytes, stream);
+}
+
+size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads,
+                                         int32_t d_head, int32_t max_shared_blocks) {
+  if (num_seqs <= 0 || num_seqs > pkv::kSplitMaxSeqs || n_heads <= 0 || d_head <= 0 ||
+      !valid_group(n_heads, n_kv_heads) || max_shared_blocks < 0)
+    return 0;
+  return make_plan(num_seqs, 1, n_heads, n_kv_heads, d_head, 1, 0, max_shared_blocks).bytes;
+}
+
+int32_t pkv_paged_decode_attention_shared_prefix(
+    void* out, const void* q, const void* k_pool, const void* v_pool,
+    const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_group,
+    const int32_t* group_blocks, int32_t n_groups, int32_t max_group_size,
+    int32_t max_shared_blocks, int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+    int32_t d_head, float scale, int32_t dtype, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !seq_group ||
+      !group_blocks)
+    return PKV_ERR_NULL;
+  int32_t st = check_pool_args(num_seqs, max_blocks_per_seq, num_blocks, max_context_len,
+                               block_size, n_kv_heads, d_head, dtype);
+  if (st != PKV_OK) return st;
+  if (!valid_group(n_heads, n_kv_heads)) return PKV_ERR_GROUP;
+  if (!std::isfinite(scale)) return PKV_ERR_SHAPE;
+  if (num_seqs > pkv::kSplitMaxSeqs || n_groups < 1 || n_groups > 65535 || max_group_size < 1 ||
+      max_group_size > num_seqs || max_shared_blocks < 0 || max_shared_blocks > max_blocks_per_seq)
+    return PKV_ERR_SHAPE;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_ERR_ALIGN;
+  const size_t eb = (size_t)elem_bytes(dtype);
+  const size_t out_bytes = (size_t)num_seqs * n_heads * d_head * eb;
+  const size_t pool_bytes = (size_t)num_blocks * pkv::kBlockTokens * n_kv_heads * d_head * eb;
+  if (overlaps(out, out_bytes, q, out_bytes) || overlaps(out, out_bytes, k_pool, pool_bytes) ||
+      overlaps(out, out_bytes, v_pool, pool_bytes))
+    return PKV_ERR_ALIAS;
+  const Plan plan = make_plan(num_seqs, 1, n_heads, n_kv_heads, d_head, max_context_len, 0,
+                              max_shared_blocks);
+  if (!workspace || workspace_bytes < plan.bytes || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
+  const int32_t g = n_heads / n_kv_heads;
+  const int64_t sets = ((int64_t)max_group_size * g + pkv::kPrefixColumns - 1) / pkv::kPrefixColumns;
+  if ((int64_t)n_groups * sets > 65535) return PKV_ERR_SHAPE;   // grid z limit
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = static_cast<const char*>(k_pool);
+  a.v_pool = static_cast<const char*>(v_pool);
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.n_heads = n_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.q_len = 1;
+  a.split = 1;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);   // log2(e)
+  a.seq_group = seq_group;
+  a.group_blocks = group_blocks;
+  a.n_groups = n_groups;
+  a.prefix_parts = plan.prefix_parts;
+  a.prefix_sets = (int32_t)sets;
+  a.max_group_size = max_group_size;
+  a.max_shared_blocks = max_shared_blocks;
+  char* ws = static_cast<char*>(workspace);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { char* p = ws + off; off += align256(bytes); return p; };
+  a.ws_prefix = reinterpret_cast<int32_t*>(take(plan.prefix_ints * sizeof(int32_t)));
+  a.ws_m = reinterpret_cast<float*>(take(plan.records * sizeof(float)));
+  a.ws_l = reinterpret_cast<float*>(take(plan.records * sizeof(float)));
+  a.ws_o = reinterpret_cast<float*>(take(plan.records * d_head * sizeof(float)));
+  a.ws_pm = reinterpret_cast<float*>(take(plan.shared_records * sizeof(float)));
+  a.ws_pl = reinterpret_cast<float*>(take(plan.shared_records * sizeof(float)));
+  a.ws_po = reinterpret_cast<float*>(take(plan.shared_records * d_head * sizeof(float)));
+  a.ws_flags = reinterpret_cast<int32_t*>(take(plan.flag_ints * sizeof(int32_t)));
+  const hipError_t e = pkv::launch_shared_prefix(a, dtype, d_head, g, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -122,17 +122,20 @@ struct Tile {
   unsigned v[4][Geo<DT, D>::kVW];
 };
 
+// kblk / vblk: the block's base in the K and V pools (the same for the whole wave, so it
+// lives in scalar registers); k_lane / v_lane: this lane's byte offsets inside the block,
+// which fit 32 bits (a block is at most 16 * 256 * 128 * 4 bytes), so each load is the
+// scalar-base + 32-bit-offset form and needs no 64-bit address arithmetic per lane.
 template <int DT, int D>
 __device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kblk, const char* vblk,
-                                          size_t k_lane, size_t v_lane, size_t tok_stride) {
+                                          uint32_t k_lane, uint32_t v_lane, uint32_t tok_stride) {
   using G_ = Geo<DT, D>;
-  const char* kp = kblk + k_lane;
 #pragma unroll
-  for (int kk = 0; kk < G_::kNK; ++kk) t.k[kk] = *reinterpret_cast<const u32x4*>(kp + 64 * kk);
-  const char* vp = vblk + v_lane;
+  for (int kk = 0; kk < G_::kNK; ++kk)
+    t.k[kk] = *reinterpret_cast<const u32x4*>(kblk + (k_lane + 64u * kk));
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const char* src = vp + jj * tok_stride;
+    const char* src = vblk + (v_lane + jj * tok_stride);
     if constexpr (G_::kVW == 8) {
       const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
       const u32x4 a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + 1);
@@ -263,16 +266,16 @@ __device__ __forceinline__ void store_row_chunk(void* base, size_t idx, const fl
 // table entries are preloaded 64 at a time into a VGPR, K/V of the next kDepth blocks are
 // in flight while `process(tile, first_token_of_block)` runs on the current one. bad is set
 // if a table entry is outside the pool (the data of that block is then not read).
-template <int DT, int D, typename F>
+template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, typename F>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
                                               int n_my, int lane, int& bad, F&& process) {
   using G_ = Geo<DT, D>;
   const int r = lane >> 4, c = lane & 15;
-  const size_t tok_stride = (size_t)a.n_kv_heads * G_::kRow;        // bytes between tokens
-  const size_t blk_stride = tok_stride * kBlockTokens;
-  const size_t head_off = (size_t)j * G_::kRow;
-  const size_t k_lane = head_off + c * tok_stride + 16 * r;
-  const size_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
+  const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;    // bytes between tokens
+  const size_t blk_stride = (size_t)tok_stride * kBlockTokens;
+  const uint32_t head_off = (uint32_t)j * G_::kRow;
+  const uint32_t k_lane = head_off + c * tok_stride + 16 * r;
+  const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
   const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_begin;
 
   int tbl = 0;   // lane i holds the table entry of block (chunk * 64 + i) of the range
@@ -289,7 +292,6 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
                      k_lane, v_lane, tok_stride);
   };
 
-  constexpr int kDepth = G_::kDepth;
   constexpr int NB = kDepth + 1;
   Tile<DT, D> tt[NB];
   load_table(0);
@@ -342,10 +344,12 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
 // Several new tokens per sequence (q_len = QL > 1): the 16 MFMA columns are the pairs
 // (new query i, head h), column c = i * G + h, C = G * QL <= 16. Query i of sequence b sees
 // tokens 0 .. N_b - QL + i (the causal mask of "09-inference-optimization", KV Cache). With
-// every column in use, P.V also runs on the matrix cores (v_mfma_f32_16x16x4_f32): for load
-// jj, lane (r, c) holds V[token 4r+jj][d = EPL*c + e] — the A operand of instance e — and
-// P[column c][token 4r+jj], its own softmax output — the B operand. No broadcast is needed;
-// the result lands as O[column c][d = EPL*(4r'+i) + e] in accumulator e, element i.
+// every column in use, P.V also runs on the matrix cores: lane (r, c) holds
+// V[tokens 4r..4r+3][d = EPL*c + e] — the A operand of instance e — and
+// P[column c][tokens 4r..4r+3], its own softmax output — the B operand (fp32:
+// v_mfma_f32_16x16x4_f32, one token per instance; 16-bit types: one 16x16x16 instance per
+// e over the whole block). No broadcast is needed; the result lands as
+// O[column c][d = EPL*(4r'+i) + e] in accumulator e, element i.
 // ---------------------------------------------------------------------------------------
 
 template <int DT, int D>
@@ -397,23 +401,74 @@ __device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = exp2_fast(s[i] - m_use);
-  st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  st.m = m_new;
 #pragma unroll
   for (int e = 0; e < G_::kEPL; ++e) st.o[e] *= alpha;
+  const bool tail = blk_tok0 + kBlockTokens > tok_end;
+  if constexpr (DT == 0) {
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    float v[G_::kEPL];
-    widen<DT, G_::kVW>(t.v[jj], v);
-    if (blk_tok0 + kBlockTokens > tok_end) {
-      const bool valid = tok0 + jj < tok_end;
+    for (int jj = 0; jj < 4; ++jj) {
+      float v[G_::kEPL];
+      widen<DT, G_::kVW>(t.v[jj], v);
+      if (tail) {
+        const bool valid = tok0 + jj < tok_end;
 #pragma unroll
-      for (int e = 0; e < G_::kEPL; ++e) v[e] = valid ? v[e] : 0.f;   // unused slots may hold NaN
+        for (int e = 0; e < G_::kEPL; ++e) v[e] = valid ? v[e] : 0.f;   // unused slots may hold NaN
+      }
+#pragma unroll
+      for (int e = 0; e < G_::kEPL; ++e)
+        st.o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[e], p[jj], st.o[e], 0, 0, 0);
+    }
+  } else {
+    // 16-bit storage: P is rounded to the storage type and multiplied into V with
+    // v_mfma_f32_16x16x16_{bf16,f16}, whose K = 16 is the block's 16 tokens. Lane (r, c)
+    // supplies A = V[tokens 4r..4r+3][d = EPL*c + e] and B = P[tokens 4r..4r+3][column c];
+    // the running sum takes the rounded P, so O / l stays a convex combination of V rows.
+    unsigned pw[2];
+    if constexpr (DT == 2) {
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 p01 = {(__bf16)p[0], (__bf16)p[1]}, p23 = {(__bf16)p[2], (__bf16)p[3]};
+      pw[0] = __builtin_bit_cast(unsigned, p01);
+      pw[1] = __builtin_bit_cast(unsigned, p23);
+      st.l = st.l * alpha + ((as_f(pw[0] << 16) + as_f(pw[0] & 0xFFFF0000u)) +
+                             (as_f(pw[1] << 16) + as_f(pw[1] & 0xFFFF0000u)));
+    } else {
+      const f16x2 p01 = {(_Float16)p[0], (_Float16)p[1]}, p23 = {(_Float16)p[2], (_Float16)p[3]};
+      pw[0] = __builtin_bit_cast(unsigned, p01);
+      pw[1] = __builtin_bit_cast(unsigned, p23);
+      st.l = st.l * alpha + (((float)p01[0] + (float)p01[1]) + ((float)p23[0] + (float)p23[1]));
+    }
+    const u32x2 pb = {pw[0], pw[1]};
+    unsigned w[4][G_::kVW];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bool valid = !tail || tok0 + jj < tok_end;      // unused slots may hold NaN
+#pragma unroll
+      for (int x = 0; x < G_::kVW; ++x) w[jj][x] = valid ? t.v[jj][x] : 0u;
     }
 #pragma unroll
-    for (int e = 0; e < G_::kEPL; ++e)
-      st.o[e] = __builtin_amdgcn_mfma_f32_16x16x4f32(v[e], p[jj], st.o[e], 0, 0, 0);
+    for (int e = 0; e < G_::kEPL; ++e) {
+      const int x = e >> 1;
+      u32x2 va;
+      if (e & 1) {      // high halves of the four tokens' word x
+        va[0] = (w[1][x] & 0xFFFF0000u) | (w[0][x] >> 16);
+        va[1] = (w[3][x] & 0xFFFF0000u) | (w[2][x] >> 16);
+      } else {          // low halves
+        va[0] = (w[1][x] << 16) | (w[0][x] & 0xFFFFu);
+        va[1] = (w[3][x] << 16) | (w[2][x] & 0xFFFFu);
+      }
+      if constexpr (DT == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        st.o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            __builtin_bit_cast(bf16x4, va), __builtin_bit_cast(bf16x4, pb), st.o[e], 0, 0, 0);
+      } else {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        st.o[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(f16x4, va), __builtin_bit_cast(f16x4, pb), st.o[e], 0, 0, 0);
+      }
+    }
   }
+  st.m = m_new;
 }
 
 // Output row of column c of KV head j: [b][i][j*G + h] in the [B, q_len, H] row layout.
@@ -582,6 +637,23 @@ __device__ __forceinline__ bool valid_len(const DecodeArgs& a, int n) {
   return n >= a.q_len && n <= a.max_context_len;
 }
 
+// Shared blocks skipped by the split pass for sequence b (0 without a group); -1 when the
+// group id or its block count is out of range, or the shared blocks leave no private
+// token (the new token never lives in a shared block).
+__device__ __forceinline__ int shared_blocks_of(const DecodeArgs& a, int b, int n_ctx) {
+  if (!a.seq_group) return 0;
+  const int g = a.seq_group[b];
+  if (g < 0) return 0;
+  if (g >= a.n_groups) return -1;
+  const int sb = a.group_blocks[g];
+  return (sb < 0 || sb > a.max_blocks_per_seq || (long long)sb * kBlockTokens >= n_ctx) ? -1 : sb;
+}
+
+// Usable sequence for the split pass: its length is valid and its group (if any) is.
+__device__ __forceinline__ bool usable(const DecodeArgs& a, int b, int n_ctx) {
+  return valid_len(a, n_ctx) && shared_blocks_of(a, b, n_ctx) >= 0;
+}
+
 // Fixed partitions: workgroup = NW waves = KV heads hg*NW .. hg*NW+NW-1 of one
 // (partition, sequence); grid (head groups, partitions, sequences).
 template <int DT, int D, int G, int NW, bool MQ>
@@ -631,7 +703,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   for (int s = s0; s < s1; ++s) {
     const int n = a.context_lens[s];
     sm_pref[s] = run;
-    run += valid_len(a, n) ? (n + kBlockTokens - 1) / kBlockTokens : 0;
+    run += usable(a, s, n) ? (n + kBlockTokens - 1) / kBlockTokens - shared_blocks_of(a, s, n) : 0;
   }
   sm_scan[tid] = run;
   __syncthreads();
@@ -655,8 +727,8 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   if (w == 0)
     for (int s = tid; s <= B; s += kThreads) a.ws_prefix[s] = sm_pref[s];
   const int rows_per_seq = a.q_len * a.n_heads;
-  for (int s = w; s < B; s += gridDim.x)        // invalid lengths: NaN outputs
-    if (!valid_len(a, a.context_lens[s]))
+  for (int s = w; s < B; s += gridDim.x)        // invalid lengths or groups: NaN outputs
+    if (!usable(a, s, a.context_lens[s]))
       write_nan_rows<DT, D>(a, (size_t)s * rows_per_seq, rows_per_seq, tid, kThreads);
   if (w >= W) return;
   const int C = G * a.q_len;
@@ -671,16 +743,19 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
       if (sm_pref[mid] <= rem) lo = mid; else hi = mid;
     }
     const int b = lo;
-    const int blk0 = rem - sm_pref[b];
+    const int n_ctx = a.context_lens[b];
+    const int skip = shared_blocks_of(a, b, n_ctx);   // >= 0: b has units
+    const int blk0 = rem - sm_pref[b];                // within the unshared blocks
     const int nb = sm_pref[b + 1] - sm_pref[b];
     const long long seg_end = min(u1, (long long)hg * T1 + sm_pref[b + 1]);
     const int n_my = (int)(seg_end - u);
     const int j = hg * NW + wave;
     if (j < a.n_kv_heads) {
-      const int n_ctx = a.context_lens[b];
-      const int tok_end = min(n_ctx, (blk0 + n_my) * kBlockTokens);
+      const int tok_end = min(n_ctx, (skip + blk0 + n_my) * kBlockTokens);
       const size_t rec0 = ((size_t)(w + (long long)hg * B + b) * NW + wave) * C;
-      run_segment<DT, D, G, MQ>(a, b, j, blk0, n_my, tok_end, n_ctx, blk0 == 0 && n_my == nb,
+      // a sequence with a shared prefix always leaves a record: the merge adds the prefix
+      run_segment<DT, D, G, MQ>(a, b, j, skip + blk0, n_my, tok_end, n_ctx,
+                                skip == 0 && blk0 == 0 && n_my == nb && !(a.seq_group && a.seq_group[b] >= 0),
                                 lane, [&](int c) { return rec0 + c; });
     }
     u = seg_end;
@@ -689,7 +764,8 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
 
 // One workgroup per output row (sequence b, new query i, head h): combine that row's
 // records by the rescale rule. Fixed mode: the partitions. Split mode: the segments of its
-// stream.
+// stream, then, for a grouped sequence, its shared-prefix records. The records form two
+// arithmetic runs, (base, stride, n_rec) and (pbase, 1, n_pre), each read by its own loop.
 template <int DT, int D, int NW>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int Q4 = D / 4;          // float4 chunks per output row
@@ -701,10 +777,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const int h = row - b * per_seq - i * a.n_heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n_ctx = a.context_lens[b];
-  if (!valid_len(a, n_ctx)) return;                      // decode wrote NaN
+  if (!usable(a, b, n_ctx)) return;                      // decode wrote NaN
 
-  size_t base, stride;
-  int n_rec;
+  size_t base, stride, pbase = 0;
+  int n_rec, n_pre = 0;
+  int nan_row = 0;
   if (a.split) {
     const int B = a.num_seqs;
     const int G = a.n_heads / a.n_kv_heads;
@@ -720,10 +797,26 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     // workgroup owning unit x: the largest w with w*T/W <= x
     const long long first = ((U + 1) * W - 1) / T;
     const long long last = ((U + nb) * W - 1) / T;
-    if (first == last) return;                              // decode wrote the output
+    const int grp = a.seq_group ? a.seq_group[b] : -1;
+    if (first == last && grp < 0) return;                   // decode wrote the output
     n_rec = (int)(last - first + 1);
     base = ((size_t)(first + (long long)hg * B + b) * NW + wv) * C + (size_t)i * G + hh;
     stride = (size_t)NW * C;
+    if (grp >= 0) {
+      const int sb = a.group_blocks[grp];                   // <= max_blocks_per_seq here
+      if (sb > a.max_shared_blocks) {
+        nan_row = 1;
+      } else {
+        n_pre = (sb * kBlockTokens + kPrefixPartition - 1) / kPrefixPartition;
+        pbase = ((size_t)b * a.n_heads + h) * a.prefix_parts;
+        for (int p = tid; p < n_pre; p += 256) nan_row |= a.ws_flags[(size_t)b * a.prefix_parts + p];
+      }
+      // the group broke its promise (see prefix_kernel): NaN row
+      if (__syncthreads_or(nan_row)) {
+        for (int x = tid; x < D; x += 256) store_elem<DT>(a.out, (size_t)row * D + x, __builtin_nanf(""));
+        return;
+      }
+    }
   } else {
     n_rec = (n_ctx + a.partition_tokens - 1) / a.partition_tokens;
     if (n_rec <= 1) return;                                 // decode wrote the output
@@ -735,7 +828,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   __shared__ f32x4 part[PR][Q4];
 
   float mx = -INFINITY;
-  for (int i = tid; i < n_rec; i += 256) mx = fmaxf(mx, a.ws_m[base + i * stride]);
+  for (int k = tid; k < n_rec; k += 256) mx = fmaxf(mx, a.ws_m[base + k * stride]);
+  for (int k = tid; k < n_pre; k += 256) mx = fmaxf(mx, a.ws_pm[pbase + k]);
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
   if (lane == 0) red[wave] = mx;
@@ -744,10 +838,12 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   __syncthreads();
 
   float sum = 0.f;
-  for (int i = tid; i < n_rec; i += 256) {
-    const size_t rec = base + i * stride;
-    sum = fmaf(a.ws_l[rec], exp2_fast(a.ws_m[rec] - M), sum);
+  for (int k = tid; k < n_rec; k += 256) {
+    const size_t r = base + k * stride;
+    sum = fmaf(a.ws_l[r], exp2_fast(a.ws_m[r] - M), sum);
   }
+  for (int k = tid; k < n_pre; k += 256)
+    sum = fmaf(a.ws_pl[pbase + k], exp2_fast(a.ws_pm[pbase + k] - M), sum);
 #pragma unroll
   for (int s = 32; s > 0; s >>= 1) sum += __shfl_xor(sum, s);
   if (lane == 0) red[wave] = sum;
@@ -757,10 +853,15 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   const int q = tid % Q4, pr = tid / Q4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int i = pr; i < n_rec; i += PR) {
-    const size_t rec = base + i * stride;
-    const float f = exp2_fast(a.ws_m[rec] - M);
-    acc += f * reinterpret_cast<const f32x4*>(a.ws_o + rec * D)[q];
+  for (int k = pr; k < n_rec; k += PR) {
+    const size_t r = base + k * stride;
+    const float f = exp2_fast(a.ws_m[r] - M);
+    acc += f * reinterpret_cast<const f32x4*>(a.ws_o + r * D)[q];
+  }
+  for (int k = pr; k < n_pre; k += PR) {
+    const size_t r = pbase + k;
+    const float f = exp2_fast(a.ws_pm[r] - M);
+    acc += f * reinterpret_cast<const f32x4*>(a.ws_po + r * D)[q];
   }
   part[pr][q] = acc;
   __syncthreads();
@@ -771,6 +872,118 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     const float inv = 1.0f / L;
 #pragma unroll
     for (int x = 0; x < 4; ++x) store_elem<DT>(a.out, (size_t)row * D + 4 * tid + x, t[x] * inv);
+  }
+}
+
+
+// Shared-prefix pass. Workgroup = 4 waves on KV head j of prefix partition p
+// (kPrefixPartition tokens) of group g, column set cs; wave w owns the 16 columns
+// k = cs * 64 + 16 * w + c (lane column c), column k being the pair (member m = k / G,
+// head h = k % G), members being the sequences of group g in increasing order. Every wave
+// reads its partition's K/V blocks through the first member's table (the four waves read
+// the same bytes, so HBM sees them once) and runs them against its query tile with the
+// multi-query block processor (no causal limit: every shared token is visible to every
+// member). The workgroups of KV head 0 and column set 0 also compare every member's table
+// with the first member's over their partition and leave one flag per (member, partition)
+// for the merge.
+// Blocks in flight per prefix-pass wave: K and V of one block take 4 * kNK + 4 * kVW
+// registers per lane; about 200 registers go to prefetch.
+template <int DT, int D>
+constexpr int kPrefixDepth = 200 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) - 1;
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(256) void prefix_kernel(DecodeArgs a) {
+  using G_ = Geo<DT, D>;
+  const int p = blockIdx.x, j = blockIdx.y;
+  const int g = blockIdx.z / a.prefix_sets, cs = blockIdx.z - g * a.prefix_sets;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int B = a.num_seqs;
+  __shared__ int sm_members[kSplitMaxSeqs];
+  __shared__ int sm_scan[256];
+
+  const int sb = a.group_blocks[g];
+  if (sb <= 0 || sb > a.max_blocks_per_seq || sb > a.max_shared_blocks) return;
+  constexpr int kPartBlocks = kPrefixPartition / kBlockTokens;
+  const int blk_begin = p * kPartBlocks;
+  const int blk_end = min(sb, blk_begin + kPartBlocks);
+  if (blk_begin >= blk_end) return;                        // uniform: before any barrier
+
+  // Members of g, in sequence order (chunked count, prefix sum, scatter).
+  const int chunk = (B + 255) / 256;
+  const int s0 = min(B, tid * chunk), s1 = min(B, s0 + chunk);
+  int cnt = 0;
+  for (int s = s0; s < s1; ++s) cnt += a.seq_group[s] == g;
+  sm_scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int v = tid >= off ? sm_scan[tid - off] : 0;
+    __syncthreads();
+    sm_scan[tid] += v;
+    __syncthreads();
+  }
+  int pos = tid > 0 ? sm_scan[tid - 1] : 0;
+  for (int s = s0; s < s1; ++s)
+    if (a.seq_group[s] == g) sm_members[pos++] = s;
+  const int M = sm_scan[255];
+  __syncthreads();
+  if (M == 0) return;
+  const int leader = sm_members[0];
+  const int32_t* lead_row = a.block_tables + (size_t)leader * a.max_blocks_per_seq;
+  const bool too_many = M > a.max_group_size;
+
+  if (j == 0 && cs == 0) {          // uniform over the workgroup
+    // one (member, block) pair per thread and step, so the table reads go out together
+    __shared__ int sm_flag[kSplitMaxSeqs];
+    const int nblk = blk_end - blk_begin;
+    for (int m = tid; m < M; m += 256) sm_flag[m] = too_many;
+    __syncthreads();
+#pragma unroll 4
+    for (int x = tid; x < M * nblk; x += 256) {
+      const int m = x / nblk, k = blk_begin + (x - m * nblk);
+      if (a.block_tables[(size_t)sm_members[m] * a.max_blocks_per_seq + k] != lead_row[k])
+        sm_flag[m] = 1;            // every writer stores the same value
+    }
+    __syncthreads();
+    for (int m = tid; m < M; m += 256)
+      a.ws_flags[(size_t)sm_members[m] * a.prefix_parts + p] = sm_flag[m];
+  }
+  const int k0 = cs * 16 * kPrefixWaves + 16 * wave;       // first column of this wave
+  if (too_many || k0 >= M * G) return;                     // no barrier below
+  const int tok_end = blk_end * kBlockTokens;
+
+  const int k = k0 + c;
+  const bool used = k < M * G;
+  u32x4 qf[G_::kNK];
+  load_query<DT, D>(a, used, used ? (size_t)sm_members[k / G] * a.n_heads + (size_t)j * G + k % G : 0,
+                    r, qf);
+  MqState<DT, D> st;
+  int bad = 0;
+  // The four waves read the same blocks, so each keeps more of them in flight than a
+  // decode wave does.
+  stream_blocks<DT, D, kPrefixDepth<DT, D>>(a, leader, j, blk_begin, blk_end - blk_begin, lane, bad,
+                                            [&](const Tile<DT, D>& tl, int tok0) {
+    process_block_mq<DT, D>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
+  });
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+  if (!used) return;
+  const float qnan = __builtin_nanf("");
+  const int b = sm_members[k / G];
+  const size_t idx = ((size_t)b * a.n_heads + (size_t)j * G + k % G) * a.prefix_parts + p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float* dst = a.ws_po + idx * D + G_::kEPL * (4 * r + i);
+#pragma unroll
+    for (int e = 0; e < G_::kEPL; e += 4) {
+      const f32x4 x = {bad ? qnan : st.o[e][i], bad ? qnan : st.o[e + 1][i],
+                       bad ? qnan : st.o[e + 2][i], bad ? qnan : st.o[e + 3][i]};
+      *reinterpret_cast<f32x4*>(dst + e) = x;
+    }
+  }
+  if (r == 0) {
+    a.ws_pm[idx] = bad ? qnan : st.m;
+    a.ws_pl[idx] = bad ? qnan : st.l;
   }
 }
 
@@ -844,7 +1057,44 @@ hipError_t launch_dim(const DecodeArgs& a, int d_head, int group, hipStream_t st
   return hipErrorInvalidValue;
 }
 
+template <int DT, int D, int G>
+hipError_t launch_prefix_typed(DecodeArgs a, hipStream_t stream) {
+  const dim3 pgrid(a.prefix_parts, a.n_kv_heads, a.n_groups * a.prefix_sets);
+  hipLaunchKernelGGL((prefix_kernel<DT, D, G>), pgrid, dim3(64 * kPrefixWaves), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_waves<DT, D, G>(a, stream);      // split pass + merge (a.split == 1)
+}
+
+template <int DT, int D>
+hipError_t launch_prefix_group(const DecodeArgs& a, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_prefix_typed<DT, D, 1>(a, stream);
+    case 2: return launch_prefix_typed<DT, D, 2>(a, stream);
+    case 4: return launch_prefix_typed<DT, D, 4>(a, stream);
+    case 8: return launch_prefix_typed<DT, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_prefix_dim(const DecodeArgs& a, int d_head, int group, hipStream_t stream) {
+  if (d_head == 64) return launch_prefix_group<DT, 64>(a, group, stream);
+  if (d_head == 128) return launch_prefix_group<DT, 128>(a, group, stream);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_shared_prefix(const DecodeArgs& a, int dtype, int d_head, int group,
+                                hipStream_t stream) {
+  switch (dtype) {
+    case 0: return launch_prefix_dim<0>(a, d_head, group, stream);
+    case 1: return launch_prefix_dim<1>(a, d_head, group, stream);
+    case 2: return launch_prefix_dim<2>(a, d_head, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d_head, int group, hipStream_t stream) {
   switch (dtype) {

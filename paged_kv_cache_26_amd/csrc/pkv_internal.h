@@ -8,10 +8,14 @@
 namespace pkv {
 
 constexpr int kBlockTokens = 16;   // tokens per KV block (the only supported block size)
+constexpr int kMaxKvHeads = 256;   // keeps byte offsets inside a block within 32 bits
 constexpr int kFallbackPartition = 512;   // fixed partition size when the split mode cannot run
 constexpr int kSplitMaxSeqs = 4096;       // split mode keeps the per-sequence prefix in LDS
 constexpr int kSplitMaxWorkgroups = 1024; // upper bound of the split-mode grid
-constexpr int kSplitMinBlocks = 16;       // fewest blocks a split-mode workgroup is given
+constexpr int kSplitMinBlocks = 8;        // fewest blocks a split-mode workgroup is given
+constexpr int kPrefixPartition = 512;     // tokens per prefix-pass partition
+constexpr int kPrefixWaves = 4;           // prefix-pass waves per workgroup, 16 columns each
+constexpr int kPrefixColumns = 16 * kPrefixWaves;
 
 // Waves per decode workgroup (one KV head each) used with this many KV heads. The
 // launcher may use fewer (4) for kernels that do not fit 256 registers per lane; this is
@@ -59,6 +63,20 @@ struct DecodeArgs {
   int32_t split;                     // 1: balanced split over the GPU; 0: fixed partitions
   int32_t partition_tokens, max_partitions;   // fixed mode
   int32_t split_workgroups;          // split mode: grid size W (set by the launcher)
+  // Shared prefixes (optional, split mode, q_len 1): seq_group[b] is the group of
+  // sequence b (-1: none); the members of group g share their first group_blocks[g]
+  // table entries. The prefix pass reads those blocks once per group and leaves records
+  // ws_p* at (b * n_heads + h) * prefix_parts + p; the split pass covers the rest.
+  const int32_t* seq_group;
+  const int32_t* group_blocks;
+  int32_t n_groups, prefix_parts, prefix_sets;
+  int32_t max_group_size, max_shared_blocks;  // host bounds the prefix grid was sized for
+  float* ws_pm;
+  float* ws_pl;
+  float* ws_po;
+  int32_t* ws_flags;                 // [num_seqs * prefix_parts] nonzero: member b's table
+                                     // disagrees with the group's in partition p, or the
+                                     // group has more than max_group_size members
   float scale_log2;                  // scale * log2(e): scores are kept in base 2
 };
 
@@ -67,5 +85,8 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 // dtype: 0 f32, 1 f16, 2 bf16; d_head 64/128; group 1/2/4/8 (validated by the caller).
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d_head, int group,
                          hipStream_t stream);
+// Shared-prefix decode (split mode, q_len 1): prefix pass, split pass, merge.
+hipError_t launch_shared_prefix(const DecodeArgs& a, int dtype, int d_head, int group,
+                                hipStream_t stream);
 
 }  // namespace pkv

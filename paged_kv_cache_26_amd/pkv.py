@@ -45,6 +45,10 @@ _SIGNATURES = {
                                                  _c_i32, _c_ptr, _c_size, _c_ptr]),
     "pkv_multi_query_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                   _c_i32]),
+    "pkv_paged_decode_attention_shared_prefix": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 11 +
+                                                 [ctypes.c_float, _c_i32, _c_ptr, _c_size,
+                                                  _c_ptr]),
+    "pkv_shared_prefix_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     # block manager (include/pkv_block_manager.h)
     "pkv_bm_create": (_c_ptr, [_c_i32, _c_i32, _c_ptr]),
     "pkv_bm_destroy": (None, [_c_ptr]),
@@ -62,6 +66,8 @@ _SIGNATURES = {
     "pkv_bm_tables": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_ptr]),
     "pkv_copy_blocks": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  _c_i32, _c_ptr]),
+    "pkv_find_shared_prefixes": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr,
+                                          _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -232,6 +238,45 @@ def pkv_paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, contex
         _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_paged_multi_query_attention")
+    return out
+
+
+def pkv_shared_prefix_workspace_bytes(num_seqs: int, n_heads: int, n_kv_heads: int,
+                                      d_head: int, max_shared_blocks: int) -> int:
+    return int(load_library().pkv_shared_prefix_workspace_bytes(num_seqs, n_heads, n_kv_heads,
+                                                                d_head, max_shared_blocks))
+
+
+def pkv_paged_decode_attention_shared_prefix(out, q, k_pool, v_pool, block_tables, context_lens,
+                                             seq_group, group_blocks, max_group_size: int,
+                                             max_shared_blocks: int, max_context_len: int,
+                                             scale: float | None = None, workspace=None,
+                                             stream=None):
+    """pkv_paged_decode_attention with groups sharing leading blocks read once per group.
+
+    seq_group [B] int32 (group id or -1), group_blocks [n_groups] int32 (shared blocks).
+    """
+    lib = load_library()
+    _check_device(out, q, k_pool, v_pool, block_tables, context_lens, seq_group, group_blocks)
+    _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype,
+             "q, out and pools must share a supported dtype")
+    _require(seq_group.dtype == torch.int32 and group_blocks.dtype == torch.int32,
+             "seq_group and group_blocks must be int32")
+    B, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = pkv_shared_prefix_workspace_bytes(B, H, k_pool.shape[2], d, max_shared_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.pkv_paged_decode_attention_shared_prefix(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
+        _ptr(seq_group), _ptr(group_blocks), group_blocks.shape[0], int(max_group_size),
+        int(max_shared_blocks), B, block_tables.shape[1], k_pool.shape[0], int(max_context_len),
+        k_pool.shape[1], H, k_pool.shape[2], d, float(scale), _DTYPE_CODE[q.dtype],
+        _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_paged_decode_attention_shared_prefix")
     return out
 
 

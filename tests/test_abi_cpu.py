@@ -109,6 +109,7 @@ def _decode_call(lib, **over):
     (dict(q=0x20004), -11),
     (dict(out=0x100000), -12),                         # out inside k_pool
     (dict(scale=float("nan")), -2),
+    (dict(H=512, Hkv=512), -2),                        # more KV heads than supported
 ])
 def test_decode_rejects_bad_arguments_on_host(lib, over, code):
     assert _decode_call(lib, **over) == code

@@ -1,0 +1,190 @@
+"""Shared-prefix decode (each group's common blocks read once) on the GPU against the fp64
+oracle, through the C ABI. The oracle is the plain paged decode attention: grouping
+changes how the shared blocks are read, not what is computed."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pkv_oracle as orc
+from paged_kv_cache_26_amd import pkv
+from paged_kv_cache_26_amd import workload as wlm
+from paged_kv_cache_26_amd.block_manager import find_shared_prefixes
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available()
+    pkv.load_library()
+
+
+def sp_workload(dtype="bf16", H=32, Hkv=8, d=128, B=8, groups=2, prefix=200, suffix=(5, 60),
+                seed=0):
+    spec = wlm.Spec(f"sp-{dtype}-{H}-{Hkv}-{d}-{B}-{groups}-{prefix}", dtype, B, H, Hkv, d,
+                    "gqa", groups=groups, prefix_len=prefix, suffix_range=suffix)
+    return wlm.make_workload(spec, seed=seed)
+
+
+def oracle_out(wl, pairs=None):
+    kp, vp = orc.kv_append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.block_tables,
+                           wl.positions, 16)
+    return orc.paged_decode_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                      wl.scale, wl.dtype, pairs=pairs)
+
+
+def gpu_shared(wl, grp=None, t=None, seq_group=None, group_blocks=None, max_group_size=None,
+               max_shared_blocks=None):
+    """Append, then the shared-prefix decode; grouping found from the tables unless given."""
+    if t is None:
+        t = wlm.to_torch(wl, DEV)
+        pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                          t["positions"])
+    if grp is None:
+        grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    sg = grp.seq_group if seq_group is None else seq_group
+    gb = grp.group_blocks if group_blocks is None else group_blocks
+    out = torch.empty_like(t["q"])
+    pkv.pkv_paged_decode_attention_shared_prefix(
+        out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"], t["context_lens"],
+        torch.from_numpy(np.ascontiguousarray(sg, np.int32)).to(DEV),
+        torch.from_numpy(np.ascontiguousarray(gb, np.int32)).to(DEV),
+        grp.max_group_size if max_group_size is None else max_group_size,
+        grp.max_shared_blocks if max_shared_blocks is None else max_shared_blocks,
+        wl.max_context_len, wl.scale)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), t
+
+
+def test_shared_prefix_small_workload():
+    _log("shared prefix: small shared-prefix workload")
+    wl = wlm.make_workload(5, small=True)
+    got, _ = gpu_shared(wl)
+    assert_close(got, oracle_out(wl), "bf16", "small shared-prefix")
+
+
+@pytest.mark.parametrize("dtype,H,Hkv,d,B,groups,prefix", [
+    ("bf16", 32, 8, 128, 12, 3, 700),      # two prefix partitions, 4 columns per member
+    ("f16", 32, 32, 128, 6, 2, 300),       # MHA: one column per member
+    ("f16", 16, 8, 64, 40, 2, 520),        # 20 members x 2 heads: one column set
+    ("bf16", 64, 8, 128, 36, 2, 100),      # 18 members x 8 heads: three column sets
+    ("f32", 8, 2, 128, 10, 2, 160),        # fp32, two query tiles per wave
+    ("f32", 8, 4, 64, 9, 3, 48),
+])
+def test_shared_prefix_shapes(dtype, H, Hkv, d, B, groups, prefix):
+    _log(f"shared prefix: {dtype} H{H} Hkv{Hkv} d{d} B{B} groups{groups} prefix{prefix}")
+    wl = sp_workload(dtype, H, Hkv, d, B, groups, prefix, seed=B + prefix)
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    assert grp.n_groups == groups
+    got, _ = gpu_shared(wl, grp)
+    assert_close(got, oracle_out(wl), dtype, "shapes")
+
+
+def test_mixed_batch_grouped_and_ungrouped():
+    """Sequences outside any group, a group sharing no whole block and a regular group in
+    one batch."""
+    _log("shared prefix: mixed batch")
+    wl = sp_workload(B=9, groups=3, prefix=150, seed=4)
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    sg = grp.seq_group.copy()
+    sg[[0, 4]] = -1                               # two sequences read their prefix themselves
+    gb = grp.group_blocks.copy()
+    gb[1] = 0                                     # group 1 shares nothing
+    got, _ = gpu_shared(wl, grp, seq_group=sg, group_blocks=gb)
+    assert_close(got, oracle_out(wl), "bf16", "mixed")
+
+
+def test_equals_plain_decode_within_bars():
+    wl = wlm.make_workload(5, small=True)
+    got, t = gpu_shared(wl)
+    out = torch.empty_like(t["q"])
+    pkv.pkv_paged_decode_attention(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                                   t["context_lens"], wl.max_context_len, wl.scale)
+    torch.cuda.synchronize()
+    assert_close(got, out.double().cpu().numpy(), "bf16", "vs plain decode")
+
+
+def test_full_size_shared_prefix_workload_sampled():
+    """128 sequences in 8 groups of 16 over a 2048-token prefix, the launch the benchmark
+    times; the oracle checks sampled (sequence, head) rows."""
+    _log("shared prefix: full-size workload")
+    wl = wlm.make_workload(5)
+    got, _ = gpu_shared(wl)
+    rng = np.random.default_rng(5)
+    seqs = sorted(rng.choice(wl.batch, size=6, replace=False).tolist())
+    pairs = [(b, h) for b in seqs for h in sorted(rng.choice(32, size=4, replace=False).tolist())]
+    ref = oracle_out(wl, pairs=pairs)
+    b = np.array([p[0] for p in pairs])
+    h = np.array([p[1] for p in pairs])
+    assert_close(got[b, h], ref[b, h], "bf16", "full size sampled")
+    assert np.isfinite(got).all()
+
+
+def test_member_with_a_different_table_gets_nan():
+    """A member whose table disagrees with the leader's inside the shared run is flagged;
+    the other members are unaffected."""
+    wl = wlm.make_workload(5, small=True)
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    members = np.flatnonzero(grp.seq_group == 0)
+    victim = int(members[2])
+    t = wlm.to_torch(wl, DEV)
+    pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                      t["positions"])
+    other = int(wl.block_tables[int(np.flatnonzero(grp.seq_group == 1)[0]), 3])
+    t["block_tables"][victim, 3] = other          # points into the other group's prefix
+    got, _ = gpu_shared(wl, grp, t=t)
+    assert np.isnan(got[victim]).all()
+    keep = [b for b in range(wl.batch) if b != victim]
+    assert_close(got[keep], oracle_out(wl)[keep], "bf16", "others")
+
+
+def test_invalid_groups_give_nan_for_their_members_only():
+    wl = sp_workload(B=12, groups=3, prefix=120, seed=8)
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    ref = oracle_out(wl)
+    # group id out of range for one sequence
+    sg = grp.seq_group.copy()
+    sg[1] = 7
+    got, _ = gpu_shared(wl, grp, seq_group=sg)
+    assert np.isnan(got[1]).all()
+    keep = [b for b in range(12) if b != 1]
+    assert_close(got[keep], ref[keep], "bf16", "bad group id")
+    # a group larger than max_group_size: all its members
+    got, _ = gpu_shared(wl, grp, max_group_size=3)
+    assert np.isnan(got).all()                    # every group has 4 members
+    # group 0 claims more blocks than max_shared_blocks: all its members; group 2 claims
+    # more blocks than a table holds: all its members
+    sb = grp.max_shared_blocks
+    gb = grp.group_blocks.copy()
+    gb[0] = sb + 1
+    gb[2] = 200
+    got, _ = gpu_shared(wl, grp, group_blocks=gb)
+    g0, g1, g2 = (grp.seq_group == g for g in range(3))
+    assert np.isnan(got[g0 | g2]).all()
+    assert_close(got[g1], ref[g1], "bf16", "good group")
+    # group 1 claims one block more than its members share: the first member's result
+    # stands (its own table was read); the others' tables differ there and give NaN
+    gb = grp.group_blocks.copy()
+    gb[1] = sb + 1
+    got, _ = gpu_shared(wl, grp, group_blocks=gb, max_shared_blocks=sb + 1)
+    first, rest = np.flatnonzero(g1)[0], np.flatnonzero(g1)[1:]
+    assert np.isnan(got[rest]).all()
+    assert_close(got[~g1], ref[~g1], "bf16", "other groups")
+    if wl.context_lens[first] > (sb + 1) * 16:
+        assert_close(got[first], ref[first], "bf16", "first member")
+    else:                                          # its last token is inside the claimed run
+        assert np.isnan(got[first]).all()
+
+
+def test_repeated_calls_bitwise_identical():
+    wl = wlm.make_workload(5, small=True)
+    a, t = gpu_shared(wl)
+    b, _ = gpu_shared(wl, t=t)
+    assert np.array_equal(a, b)
