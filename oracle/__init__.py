@@ -5,7 +5,16 @@ package; the product path never does.
 """
 from .pkv_oracle import (  # noqa: F401
     DTYPE_BYTES,
+    E4M3_MAX,
+    KV_FORMATS,
     STORAGE_DTYPES,
+    dequantize,
+    e4m3_decode,
+    e4m3_encode,
+    gather_dequantized,
+    kv_append_quantized,
+    paged_decode_attention_quantized,
+    quantize_row,
     gather_kv,
     kv_append,
     kv_bytes_per_token,

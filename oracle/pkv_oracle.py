@@ -292,3 +292,146 @@ def paged_multi_query_attention(q: np.ndarray, k_pool: np.ndarray, v_pool: np.nd
             weights = softmax_two_pass(scores)
             out[b, i, h] = weights @ vals[:visible]
     return out
+
+
+# --------------------------------------------------------------------------------------
+# Quantized KV cache. "LLM 推理优化全景实战" §4.1 gives the affine quantizer
+# Q(x) = round(x / s) + z and its inverse x^ = s * (Q(x) - z); "Scaling Book 第 11 章"
+# names FP8 and INT8 as the 8-bit choices. Readings taken where the pages are silent:
+# one (s, z) per token and KV head, computed when the token is appended; INT8 codes are
+# unsigned bytes 0..255 whose range [min(x, 0), max(x, 0)] includes zero (so zero is exact);
+# FP8 is the OCP E4M3 format (sign, 4 exponent bits with bias 7, 3 mantissa bits, no
+# infinities, S.1111.111 is NaN, largest finite 448) with s = max|x| / 448 and z = 0.
+# Every quantizer step runs in binary32, the precision the GPU kernel uses, so both sides
+# reach the same integer codes; dequantization and attention are fp64.
+# Code pools:  [num_blocks, block_size, n_kv_heads, d_head] uint8.
+# Scale pools: [num_blocks, n_kv_heads, block_size, 2] float32 holding (s, z).
+# --------------------------------------------------------------------------------------
+
+KV_FORMATS = ("int8", "fp8")
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """fp64 value of each E4M3 byte, from the field definition."""
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+_E4M3_POS = e4m3_decode(np.arange(0x7F))          # codes 0..126: the finite non-negatives
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 byte to each binary32 value (ties to the even code), saturating at
+    +-448. Found by search over the 127 finite magnitudes; the sign bit is copied."""
+    y = np.asarray(y, dtype=np.float32)
+    a = np.abs(y).astype(np.float64)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a), 1, 126)   # first value >= a
+    lo = hi - 1
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a >= E4M3_MAX, 126, pick)
+    return (pick | np.where(np.signbit(y), 0x80, 0)).astype(np.uint8)
+
+
+def quantize_row(x: np.ndarray, fmt: str):
+    """One token's row of one KV head (any float array) -> (codes uint8, s, z), binary32 steps.
+
+    int8: lo = min(min x, 0), hi = max(max x, 0), s = (hi - lo) / 255 (1 if zero),
+          z = clamp(round(-lo / s), 0, 255), Q = clamp(round(x / s) + z, 0, 255).
+    fp8:  s = max|x| / 448 (1 if zero), z = 0, Q = E4M3(x / s).
+    round is round-half-to-even.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    f255 = np.float32(255.0)
+    if fmt == "int8":
+        lo = np.minimum(np.min(x32), np.float32(0.0))
+        hi = np.maximum(np.max(x32), np.float32(0.0))
+        s = np.float32(np.float32(hi - lo) / f255)
+        if s == 0:
+            s = np.float32(1.0)
+        z = np.clip(np.rint(np.float32(-lo) / s), np.float32(0.0), f255).astype(np.float32)
+        q = np.clip(np.rint(x32 / s) + z, np.float32(0.0), f255)
+        return q.astype(np.uint8), np.float32(s), np.float32(z)
+    if fmt == "fp8":
+        amax = np.max(np.abs(x32))
+        s = np.float32(amax / np.float32(E4M3_MAX))
+        if s == 0:
+            s = np.float32(1.0)
+        return e4m3_encode(x32 / s), np.float32(s), np.float32(0.0)
+    raise ValueError(f"unknown KV format {fmt!r}")
+
+
+def dequantize(codes: np.ndarray, s, z, fmt: str) -> np.ndarray:
+    """x^ = s * (Q - z) in fp64 (for fp8, Q is the E4M3 value and z = 0). s and z broadcast
+    over the last axis of codes."""
+    s = np.asarray(s, dtype=np.float64)[..., None]
+    z = np.asarray(z, dtype=np.float64)[..., None]
+    if fmt == "int8":
+        return s * (np.asarray(codes, dtype=np.float64) - z)
+    if fmt == "fp8":
+        return s * (e4m3_decode(codes) - z)
+    raise ValueError(f"unknown KV format {fmt!r}")
+
+
+def kv_append_quantized(k_codes: np.ndarray, v_codes: np.ndarray, k_scales: np.ndarray,
+                        v_scales: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                        block_tables: np.ndarray, positions: np.ndarray, block_size: int,
+                        fmt: str, dtype: str):
+    """Copies of the code and scale pools with each sequence's new token quantized into
+    its slot (chenxutan §2.3 slot rule; quantizer above). k_new, v_new: [B, n_kv_heads,
+    d_head] in the stored dtype `dtype`."""
+    kc, vc, ks, vs = k_codes.copy(), v_codes.copy(), k_scales.copy(), v_scales.copy()
+    for b in range(k_new.shape[0]):
+        phys, off = _slot(block_tables[b], int(positions[b]), block_size)
+        for j in range(k_new.shape[1]):
+            for codes, scales, new in ((kc, ks, k_new), (vc, vs, v_new)):
+                row = storage_to_f64(new[b, j], dtype)          # exact in binary32
+                q, s, z = quantize_row(row, fmt)
+                codes[phys, off, j] = q
+                scales[phys, j, off] = (s, z)
+    return kc, vc, ks, vs
+
+
+def gather_dequantized(codes: np.ndarray, scales: np.ndarray, table_row: np.ndarray,
+                       n_tokens: int, block_size: int, kv_head: int, fmt: str) -> np.ndarray:
+    """Tokens 0..n_tokens-1 of one sequence and KV head, dequantized: [n_tokens, d_head]."""
+    t = np.arange(n_tokens, dtype=np.int64)
+    phys = np.asarray(table_row, dtype=np.int64)[t // block_size]
+    off = t % block_size
+    sz = scales[phys, kv_head, off]                          # [n_tokens, 2]
+    return dequantize(codes[phys, off, kv_head], sz[:, 0], sz[:, 1], fmt)
+
+
+def paged_decode_attention_quantized(q: np.ndarray, k_codes: np.ndarray, v_codes: np.ndarray,
+                                     k_scales: np.ndarray, v_scales: np.ndarray,
+                                     block_tables: np.ndarray, context_lens: np.ndarray,
+                                     block_size: int, scale: float, fmt: str, dtype: str,
+                                     pairs=None) -> np.ndarray:
+    """The decode attention definition (chenxutan §2.4) over dequantized K and V.
+
+    q: [B, n_heads, d_head] in the stored dtype `dtype`; pools as above, after the append.
+    Returns [B, n_heads, d_head] fp64 (NaN outside `pairs` when given)."""
+    B, n_heads, d_head = q.shape
+    n_kv_heads = k_codes.shape[2]
+    group = n_heads // n_kv_heads
+    out = np.full((B, n_heads, d_head), np.nan, dtype=np.float64)
+    wanted = {}
+    for b, h in (pairs if pairs is not None else
+                 [(b, h) for b in range(B) for h in range(n_heads)]):
+        wanted.setdefault((int(b), int(h) // group), []).append(int(h))
+    for (b, j) in sorted(wanted):
+        n_tok = int(context_lens[b])
+        keys = gather_dequantized(k_codes, k_scales, block_tables[b], n_tok, block_size, j, fmt)
+        vals = gather_dequantized(v_codes, v_scales, block_tables[b], n_tok, block_size, j, fmt)
+        for h in sorted(set(wanted[(b, j)])):
+            qh = storage_to_f64(q[b, h], dtype)
+            weights = softmax_two_pass(scale * (keys @ qh))
+            out[b, h] = weights @ vals
+    return out

@@ -14,6 +14,11 @@ Workload recipe (the same recipe is stated in the design notes):
   (fp16 via numpy, bf16 via torch's CPU conversion).
 * every slot and block not holding a token is filled with NaN ("poison"), so a kernel
   that reads outside a sequence's used slots produces NaN.
+* quantized-cache workloads (``kv_format`` "int8" / "fp8") draw each cached token's 8-bit
+  codes uniformly (E4M3 NaN bytes excluded) and its per-KV-head (s, z) from the ranges
+  below, in the same order (per sequence: K codes, K scales, V codes, V scales); unused
+  slots hold code 0x7F and NaN scales. Quantizing the new token is the method's work and
+  happens in the library (and in the oracle), not here.
 * "context length" in a workload description is the length L_b *before* the decode step.
   The step appends one token at position L_b (q_len tokens at L_b .. L_b + q_len - 1 for
   multi-query steps), then attends over N_b = L_b + q_len tokens.
@@ -209,6 +214,7 @@ class Spec:
     suffix_range: tuple | None = None  # per-sequence suffix ~ U{lo..hi}
     block_size: int = BLOCK_SIZE
     q_len: int = 1                     # new tokens (queries) per sequence this step
+    kv_format: str | None = None       # None: K/V stored in `dtype`; "int8" / "fp8" codes
 
     @property
     def group(self) -> int:
@@ -248,6 +254,46 @@ SMALL_SPECS = {
 }
 
 
+# Quantized-cache workloads: the GQA layer shape with 8-bit K/V codes and per-(token,
+# KV head) scales; q, the new tokens and the output stay bf16.
+QUANT_SPECS = {
+    "int8": Spec("gqa-int8kv", "bf16", 64, 32, 8, 128, "gqa", len_range=(4096, 8192),
+                 kv_format="int8"),
+    "fp8": Spec("gqa-fp8kv", "bf16", 64, 32, 8, 128, "gqa", len_range=(4096, 8192),
+                kv_format="fp8"),
+}
+QUANT_SMALL_SPECS = {
+    "int8": Spec("gqa-int8kv-small", "bf16", 6, 32, 8, 128, "gqa", len_range=(300, 1500),
+                 kv_format="int8"),
+    "fp8": Spec("gqa-fp8kv-small", "bf16", 6, 32, 8, 128, "gqa", len_range=(300, 1500),
+                kv_format="fp8"),
+}
+
+# Scale draws of the quantized workloads: s = base / levels * U(0.5, 1.5), so the
+# dequantized K spans about +-3 and V about +-1, like the GQA workload's N(0, 1) keys and
+# U(-1, 1) values; int8 zero points z ~ U{112..144}, fp8 z = 0.
+_QUANT_BASE = {"k": 6.0, "v": 2.0}
+_QUANT_LEVELS = {"int8": 255.0, "fp8": 448.0}
+
+
+def _draw_codes(rng, shape, fmt: str) -> np.ndarray:
+    if fmt == "int8":
+        return rng.integers(0, 256, size=shape, dtype=np.uint8)
+    u = rng.integers(0, 254, size=shape, dtype=np.int64)    # every E4M3 byte but the NaNs
+    return np.where(u < 0x7F, u, u + 1).astype(np.uint8)
+
+
+def _draw_scales(rng, shape, fmt: str, role: str) -> np.ndarray:
+    """[..., 2] float32 (s, z) for the given leading shape."""
+    base = _QUANT_BASE[role] / _QUANT_LEVELS[fmt]
+    if fmt == "fp8":
+        base *= 0.5                       # E4M3 spans +-448 around zero: half the range
+    sz = np.empty(shape + (2,), dtype=np.float32)
+    sz[..., 0] = base * rng.uniform(0.5, 1.5, size=shape)
+    sz[..., 1] = rng.integers(112, 145, size=shape) if fmt == "int8" else 0.0
+    return sz
+
+
 @dataclasses.dataclass
 class Workload:
     spec: Spec
@@ -264,6 +310,10 @@ class Workload:
     shared_tokens: int          # tokens counted more than once across sequences
     logical_k: list | None = None   # per sequence [L_b, n_kv_heads, d_head] (stored dtype)
     logical_v: list | None = None
+    # quantized caches: k_pool / v_pool hold uint8 codes and these the (s, z) pairs,
+    # [num_blocks, n_kv_heads, block_size, 2] float32
+    k_scales: np.ndarray | None = None
+    v_scales: np.ndarray | None = None
 
     # convenience -------------------------------------------------------------------------
     @property
@@ -290,16 +340,21 @@ class Workload:
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.spec.d_head)
 
+    def kv_bytes_per_token(self) -> int:
+        """K+V bytes of one token over all KV heads (codes plus (s, z) when quantized)."""
+        s = self.spec
+        if s.kv_format:
+            return 2 * s.n_kv_heads * (s.d_head + 8)
+        return 2 * s.n_kv_heads * s.d_head * DTYPE_BYTES[s.dtype]
+
     def kv_bytes_logical(self) -> int:
         """K+V bytes a decode step reads: every attended token, once per KV head."""
-        s = self.spec
-        return int(self.context_lens.sum()) * 2 * s.n_kv_heads * s.d_head * DTYPE_BYTES[s.dtype]
+        return int(self.context_lens.sum()) * self.kv_bytes_per_token()
 
     def kv_bytes_unique(self) -> int:
         """As above, with tokens shared between sequences counted once."""
-        s = self.spec
         tok = int(self.context_lens.sum()) - self.shared_tokens
-        return tok * 2 * s.n_kv_heads * s.d_head * DTYPE_BYTES[s.dtype]
+        return tok * self.kv_bytes_per_token()
 
 
 def _draw(rng, shape, dist: str, role: str) -> np.ndarray:
@@ -403,8 +458,19 @@ def make_workload(spec: Spec | int, seed: int | None = None, *, keep_logical: bo
     perm = rng.permutation(num_blocks)
     mgr = BlockManager(num_blocks, bs, free_order=perm)
 
-    k_pool = poison_pool((num_blocks, bs, Hkv, d), spec.dtype)
-    v_pool = poison_pool((num_blocks, bs, Hkv, d), spec.dtype)
+    fmt = spec.kv_format
+    if fmt is not None:
+        if spec.groups or spec.q_len != 1:
+            raise ValueError("quantized workloads are single-query without shared prefixes")
+        # codes of unused slots: 0x7F (an E4M3 NaN); their scales: NaN
+        k_pool = np.full((num_blocks, bs, Hkv, d), 0x7F, dtype=np.uint8)
+        v_pool = np.full((num_blocks, bs, Hkv, d), 0x7F, dtype=np.uint8)
+        k_scales = np.full((num_blocks, Hkv, bs, 2), np.nan, dtype=np.float32)
+        v_scales = np.full((num_blocks, Hkv, bs, 2), np.nan, dtype=np.float32)
+    else:
+        k_pool = poison_pool((num_blocks, bs, Hkv, d), spec.dtype)
+        v_pool = poison_pool((num_blocks, bs, Hkv, d), spec.dtype)
+        k_scales = v_scales = None
 
     # allocation, replayed on the real manager; data written in draw order below
     _allocate(mgr, spec, ctx, prefix_of)
@@ -449,6 +515,19 @@ def make_workload(spec: Spec | int, seed: int | None = None, *, keep_logical: bo
             if keep_logical:
                 logical_k.append(full_k)
                 logical_v.append(full_v)
+    elif fmt is not None:
+        for b in range(B):
+            nb = -(-ctx[b] // bs)
+            ids = np.asarray(tables[b, :nb], dtype=np.int64)
+            t = np.arange(ctx[b])
+            for codes, scales, role in ((k_pool, k_scales, "k"), (v_pool, v_scales, "v")):
+                c = _draw_codes(rng, (ctx[b], Hkv, d), fmt)
+                sz = _draw_scales(rng, (ctx[b], Hkv), fmt, role)
+                codes[ids[t // bs], t % bs] = c
+                scales[ids[t // bs], :, t % bs] = sz
+            if keep_logical:
+                logical_k.append(None)
+                logical_v.append(None)
     else:
         for b in range(B):
             kk = to_storage(_draw(rng, (ctx[b], Hkv, d), spec.dist, "k"), spec.dtype)
@@ -472,7 +551,8 @@ def make_workload(spec: Spec | int, seed: int | None = None, *, keep_logical: bo
     return Workload(spec=spec, seed=seed, k_pool=k_pool, v_pool=v_pool, block_tables=tables,
                     positions=positions, context_lens=positions + ql, q=q, k_new=k_new,
                     v_new=v_new, refcount=mgr.refcount_array(), shared_tokens=shared_tokens,
-                    logical_k=logical_k, logical_v=logical_v)
+                    logical_k=logical_k, logical_v=logical_v, k_scales=k_scales,
+                    v_scales=v_scales)
 
 
 def relabel_blocks(wl: Workload, seed: int) -> Workload:
@@ -492,8 +572,14 @@ def relabel_blocks(wl: Workload, seed: int) -> Workload:
     tables[used] = perm[tables[used]]
     refcount = np.empty_like(wl.refcount)
     refcount[perm] = wl.refcount
+    scales = {}
+    for name in ("k_scales", "v_scales"):
+        src = getattr(wl, name)
+        if src is not None:
+            scales[name] = np.empty_like(src)
+            scales[name][perm] = src
     return dataclasses.replace(wl, k_pool=k_pool, v_pool=v_pool, block_tables=tables,
-                               refcount=refcount)
+                               refcount=refcount, **scales)
 
 
 def to_torch(wl: Workload, device="cuda"):
@@ -505,13 +591,17 @@ def to_torch(wl: Workload, device="cuda"):
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
         return torch.from_numpy(a).to(device)
 
-    return {
+    out = {
         "k_pool": conv(wl.k_pool), "v_pool": conv(wl.v_pool),
         "k_new": conv(wl.k_new), "v_new": conv(wl.v_new), "q": conv(wl.q),
         "block_tables": torch.from_numpy(wl.block_tables).to(device),
         "positions": torch.from_numpy(wl.positions).to(device),
         "context_lens": torch.from_numpy(wl.context_lens).to(device),
     }
+    if wl.k_scales is not None:
+        out["k_scales"] = torch.from_numpy(wl.k_scales).to(device)
+        out["v_scales"] = torch.from_numpy(wl.v_scales).to(device)
+    return out
 
 
 def from_torch(t, dtype: str) -> np.ndarray:
