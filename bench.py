@@ -65,14 +65,17 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a buffer of this many MiB 3 times (a dispatch of "
                          "known traffic for scaling hardware byte counters)")
+    ap.add_argument("--kv-format", choices=["int8", "fp8"], default="int8",
+                    help="quantized cache format (--component quantized)")
     ap.add_argument("--component",
-                    choices=["decode", "block-manager", "multi-query", "shared-prefix"],
+                    choices=["decode", "block-manager", "multi-query", "shared-prefix",
+                             "quantized"],
                     default="decode",
                     help="decode: the decode step (default); block-manager: the native block "
                          "manager and the copy-on-write block copy; multi-query: q_len new "
                          "tokens per sequence (speculative verification) on the GQA workload; "
                          "shared-prefix: the shared-prefix workload with each group's common "
-                         "blocks read once")
+                         "blocks read once; quantized: the GQA workload with an 8-bit KV cache")
     ap.add_argument("--q-len", type=int, default=4, help="new tokens per sequence (multi-query)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
@@ -530,6 +533,88 @@ def run_shared_prefix(args) -> dict:
     }
 
 
+def run_quantized(args) -> dict:
+    """The GQA workload shape (64 sequences of U{4096..8192} tokens, 32 query / 8 KV heads,
+    d 128, q and out bf16) with an 8-bit KV cache: a step quantizes every new token into
+    the cache (pkv_kv_append_quantized) and runs pkv_paged_decode_attention_quantized.
+    Compared with the bf16-cache step on the same shape and lengths."""
+    import torch
+
+    from paged_kv_cache_26_amd import pkv
+    from paged_kv_cache_26_amd import workload as wlm
+
+    pkv.load_library()
+    fmt = args.kv_format
+    wl = wlm.make_workload(wlm.QUANT_SPECS[fmt], seed=3)
+    spec = wl.spec
+    dev = torch.device("cuda:0")
+    t = wlm.to_torch(wl, dev)
+    out = torch.empty_like(t["q"])
+    need = pkv.pkv_decode_workspace_bytes(wl.batch, spec.n_heads, spec.n_kv_heads, spec.d_head,
+                                          wl.max_context_len, 0)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def append():
+        pkv.pkv_kv_append_quantized(t["k_pool"], t["v_pool"], t["k_scales"], t["v_scales"],
+                                    t["k_new"], t["v_new"], t["block_tables"], t["positions"],
+                                    fmt)
+
+    def attend():
+        pkv.pkv_paged_decode_attention_quantized(out, t["q"], t["k_pool"], t["v_pool"],
+                                                 t["k_scales"], t["v_scales"], t["block_tables"],
+                                                 t["context_lens"], wl.max_context_len, fmt,
+                                                 wl.scale, 0, ws)
+
+    def step():
+        append()
+        attend()
+
+    s_step = _time_launches(step, args.steps, args.warmup)
+    s_attn = _time_launches(attend, args.steps, args.warmup)
+    del t, out, ws
+    torch.cuda.empty_cache()
+    # the same shape and lengths with a bf16 cache (workload 3, same seed)
+    ref = wlm.make_workload(3)
+    assert np.array_equal(ref.context_lens, wl.context_lens)
+    tr = wlm.to_torch(ref, dev)
+    out16 = torch.empty_like(tr["q"])
+    ws16 = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    s_bf16 = _time_launches(
+        lambda: pkv.pkv_paged_decode_attention(out16, tr["q"], tr["k_pool"], tr["v_pool"],
+                                               tr["block_tables"], tr["context_lens"],
+                                               ref.max_context_len, ref.scale, 0, ws16),
+        args.steps, args.warmup)
+    kv = wl.kv_bytes_logical()
+    tables = int(sum(-(-int(n) // 16) for n in wl.context_lens)) * 4
+    alg = kv + 2 * wl.q.nbytes + tables + 4 * wl.batch
+    gbps = alg / s_attn / 1e9
+    tokens = int(wl.context_lens.sum())
+    return {
+        "metric": f"paged decode attention over a {fmt} KV cache: KV GB/s read; us/step",
+        "value": round(kv / s_step / 1e9, 2),
+        "unit": "GB/s",
+        "higher_is_better": True,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "dtype": f"{fmt} KV, bf16 q/out",
+        "data": "synthetic (seeded)",
+        "us_per_step": round(s_step * 1e6, 2),
+        "config": {"workload": spec.name, "batch": spec.batch, "n_heads": spec.n_heads,
+                   "n_kv_heads": spec.n_kv_heads, "d_head": spec.d_head,
+                   "context_tokens": tokens, "kv_bytes_per_token": wl.kv_bytes_per_token(),
+                   "kv_bytes_per_step": kv},
+        "attention_us": round(s_attn * 1e6, 2),
+        "bf16_cache_attention_us": round(s_bf16 * 1e6, 2),
+        "speedup_vs_bf16_cache": round(s_bf16 / s_attn, 2),
+        "context_tokens_per_s": round(tokens / s_attn, 1),
+        "roofline": {"bound": "hbm", "kernel": f"{fmt}-cache decode launch (decode + merge)",
+                     "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": alg},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -546,6 +631,9 @@ def main():
         return
     if args.component == "shared-prefix":
         print(json.dumps(run_shared_prefix(args)), flush=True)
+        return
+    if args.component == "quantized":
+        print(json.dumps(run_quantized(args)), flush=True)
         return
     cfgs = [1, 2, 3, 4, 5] if args.all else [args.config]
     for cfg in cfgs:

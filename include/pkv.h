@@ -30,9 +30,10 @@
  *   * dtype is one of PKV_F32, PKV_F16, PKV_BF16; K, V, q, k_new, v_new and out share it.
  *     Arithmetic is fp32 (fp32 products and accumulation), with one exception: where
  *     the weighted sum of V runs on the matrix cores for 16 query columns at once
- *     (multi-query attention and the shared-prefix pass, 16-bit dtypes), the softmax
- *     weights are rounded to the dtype first, and the running sum uses the same
- *     rounded weights. Outputs are rounded to the dtype with round-to-nearest-even.
+ *     (multi-query attention, the shared-prefix pass and quantized caches, 16-bit
+ *     dtypes), the softmax weights (and, for quantized caches, the dequantized V) are
+ *     rounded to the dtype first, and the running sum uses the same rounded weights.
+ *     Outputs are rounded to the dtype with round-to-nearest-even.
  *   * Supported shapes: block_size == 16, d_head in {64, 128}, 1 <= n_kv_heads <= 256,
  *     n_heads / n_kv_heads in {1, 2, 4, 8}. All device pointers must be 16-byte aligned.
  *   * Return value: PKV_OK (0) or a negative PKV_ERR_* code. Errors are found on the
@@ -251,6 +252,58 @@ int32_t pkv_paged_decode_attention_shared_prefix(
  * sizes. */
 size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads,
                                          int32_t d_head, int32_t max_shared_blocks);
+
+/*
+ * Quantized KV cache (8-bit codes). Source: "LLM 推理优化全景实战" §4.1, the affine
+ * quantizer Q(x) = round(x / s) + z with dequantization x^ = s * (Q - z); "Scaling Book
+ * 第 11 章" names FP8 and INT8 as the 8-bit choices.
+ *
+ *   kv_format PKV_KV_INT8: unsigned codes 0..255; per (token, KV head) the row's range is
+ *       widened to include zero, lo = min(min x, 0), hi = max(max x, 0);
+ *       s = (hi - lo) / 255 (1 when zero), z = clamp(round(-lo / s), 0, 255),
+ *       Q = clamp(round(x / s) + z, 0, 255).
+ *   kv_format PKV_KV_FP8: OCP E4M3 codes (bias 7, 3 mantissa bits, largest 448, no
+ *       infinities); s = max|x| / 448 (1 when zero), z = 0, Q = E4M3(x / s) rounded to
+ *       nearest even and saturated at +-448.
+ *   Every quantizer step is binary32 and round() is round-half-to-even, so the codes and
+ *   (s, z) are determined bit for bit by the input row.
+ *   Code pools:  [num_blocks, block_size, n_kv_heads, d_head] uint8 (the layout of the
+ *                dtype pools with 1-byte elements).
+ *   Scale pools: [num_blocks, n_kv_heads, block_size, 2] float (s, z) per token slot.
+ */
+enum pkv_kv_format {
+  PKV_KV_INT8 = 1,
+  PKV_KV_FP8 = 2
+};
+
+/*
+ * pkv_kv_append_quantized - quantize each sequence's new K and V (one token at
+ * positions[b], as pkv_kv_append) into its slot of the code pools and its (s, z) into the
+ * scale pools. k_new, v_new [num_seqs, n_kv_heads, d_head] in dtype (f32, f16 or bf16).
+ * Sequences with an out-of-range position or table entry are skipped.
+ */
+int32_t pkv_kv_append_quantized(void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                                const void* k_new, const void* v_new,
+                                const int32_t* block_tables, const int32_t* positions,
+                                int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                int32_t block_size, int32_t n_kv_heads, int32_t d_head,
+                                int32_t dtype, int32_t kv_format, hipStream_t stream);
+
+/*
+ * pkv_paged_decode_attention_quantized - pkv_paged_decode_attention over a quantized cache:
+ * the attention of the dequantized K and V, x^ = s * (Q - z). q and out in dtype
+ * (PKV_F16 or PKV_BF16). The scores contract q with the raw codes on the matrix cores and
+ * apply s and z once per token, s (q.Q - z sum q), which equals q.x^ up to fp32 rounding;
+ * the weighted sum of V uses the dequantized values rounded to dtype (see the precision
+ * note at the top). Workspace size: pkv_decode_workspace_bytes (same arguments).
+ */
+int32_t pkv_paged_decode_attention_quantized(
+    void* out, const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    int32_t block_size, int32_t n_heads, int32_t n_kv_heads, int32_t d_head, float scale,
+    int32_t partition_tokens, int32_t dtype, int32_t kv_format, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pkv_kv_bytes_per_token - bytes one token occupies in the KV cache of a whole model:

@@ -344,7 +344,8 @@ def quantize_row(x: np.ndarray, fmt: str):
     """One token's row of one KV head (any float array) -> (codes uint8, s, z), binary32 steps.
 
     int8: lo = min(min x, 0), hi = max(max x, 0), s = (hi - lo) / 255 (1 if zero),
-          z = clamp(round(-lo / s), 0, 255), Q = clamp(round(x / s) + z, 0, 255).
+          z = clamp(round(-lo / s), 0, 255) (stored as +0 when zero),
+          Q = clamp(round(x / s) + z, 0, 255).
     fp8:  s = max|x| / 448 (1 if zero), z = 0, Q = E4M3(x / s).
     round is round-half-to-even.
     """
@@ -356,7 +357,8 @@ def quantize_row(x: np.ndarray, fmt: str):
         s = np.float32(np.float32(hi - lo) / f255)
         if s == 0:
             s = np.float32(1.0)
-        z = np.clip(np.rint(np.float32(-lo) / s), np.float32(0.0), f255).astype(np.float32)
+        # adding +0 turns a -0 (from -lo = -0.0) into +0: the stored z is never -0
+        z = np.float32(np.clip(np.rint(np.float32(-lo) / s), np.float32(0.0), f255) + np.float32(0.0))
         q = np.clip(np.rint(x32 / s) + z, np.float32(0.0), f255)
         return q.astype(np.uint8), np.float32(s), np.float32(z)
     if fmt == "fp8":

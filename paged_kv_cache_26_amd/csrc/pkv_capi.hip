@@ -114,16 +114,25 @@ bool valid_q_len(int32_t q_len, int32_t n_heads, int32_t n_kv_heads) {
 }
 
 // Shared by the single- and multi-query entry points.
+// kv_format 0: K/V pools in dtype; PKV_KV_INT8 / PKV_KV_FP8: 8-bit code pools with the
+// (s, z) pools k_scales / v_scales (q and out in dtype, which must be 16-bit).
 int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t q_len, int32_t max_blocks_per_seq, int32_t num_blocks,
                     int32_t max_context_len, int32_t block_size, int32_t n_heads,
                     int32_t n_kv_heads, int32_t d_head, float scale, int32_t partition_tokens,
-                    int32_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                    int32_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    int32_t kv_format = 0, const float* k_scales = nullptr,
+                    const float* v_scales = nullptr) {
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (kv_format != 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
   int32_t st = check_pool_args(num_seqs, max_blocks_per_seq, num_blocks, max_context_len,
                                block_size, n_kv_heads, d_head, dtype);
   if (st != PKV_OK) return st;
+  if (kv_format != 0 && ((kv_format != PKV_KV_INT8 && kv_format != PKV_KV_FP8) ||
+                         dtype == PKV_F32 || q_len != 1))
+    return PKV_ERR_DTYPE;
+  if (kv_format != 0 && (!aligned16(k_scales) || !aligned16(v_scales))) return PKV_ERR_ALIGN;
   if (!valid_group(n_heads, n_kv_heads)) return PKV_ERR_GROUP;
   if (!valid_q_len(q_len, n_heads, n_kv_heads)) return PKV_ERR_QUERIES;
   if (max_context_len < q_len) return PKV_ERR_CONTEXT;
@@ -133,9 +142,14 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
     return PKV_ERR_ALIGN;
   const size_t eb = (size_t)elem_bytes(dtype);
   const size_t out_bytes = (size_t)num_seqs * q_len * n_heads * d_head * eb;
-  const size_t pool_bytes = (size_t)num_blocks * pkv::kBlockTokens * n_kv_heads * d_head * eb;
+  const size_t pool_bytes =
+      (size_t)num_blocks * pkv::kBlockTokens * n_kv_heads * d_head * (kv_format ? 1 : eb);
+  const size_t scale_bytes = (size_t)num_blocks * pkv::kBlockTokens * n_kv_heads * 2 * sizeof(float);
   if (overlaps(out, out_bytes, q, out_bytes) || overlaps(out, out_bytes, k_pool, pool_bytes) ||
       overlaps(out, out_bytes, v_pool, pool_bytes))
+    return PKV_ERR_ALIAS;
+  if (kv_format != 0 && (overlaps(out, out_bytes, k_scales, scale_bytes) ||
+                         overlaps(out, out_bytes, v_scales, scale_bytes)))
     return PKV_ERR_ALIAS;
 
   const Plan plan = make_plan(num_seqs, q_len, n_heads, n_kv_heads, d_head, max_context_len,
@@ -171,7 +185,12 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
     a.ws_l = reinterpret_cast<float*>(ws + pre + vec);
     a.ws_o = reinterpret_cast<float*>(ws + pre + 2 * vec);
   }
-  const hipError_t e = pkv::launch_decode(a, dtype, d_head, n_heads / n_kv_heads, stream);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  const hipError_t e =
+      kv_format ? pkv::launch_decode_quantized(a, dtype, kv_format, d_head, n_heads / n_kv_heads,
+                                               stream)
+                : pkv::launch_decode(a, dtype, d_head, n_heads / n_kv_heads, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -257,6 +276,58 @@ int32_t pkv_kv_append(void* k_pool, void* v_pool, const void* k_new, const void*
   return pkv_kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, positions, num_seqs, 1,
                               max_blocks_per_seq, num_blocks, block_size, n_kv_heads, d_head,
                               dtype, stream);
+}
+
+int32_t pkv_kv_append_quantized(void* k_codes, void* v_codes, float* k_scales, float* v_scales,
+                                const void* k_new, const void* v_new,
+                                const int32_t* block_tables, const int32_t* positions,
+                                int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                int32_t block_size, int32_t n_kv_heads, int32_t d_head,
+                                int32_t dtype, int32_t kv_format, hipStream_t stream) {
+  if (!k_codes || !v_codes || !k_scales || !v_scales || !k_new || !v_new || !block_tables ||
+      !positions)
+    return PKV_ERR_NULL;
+  if (elem_bytes(dtype) == 0 || (kv_format != PKV_KV_INT8 && kv_format != PKV_KV_FP8))
+    return PKV_ERR_DTYPE;
+  if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
+  if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
+  if (num_seqs <= 0 || num_seqs > 65535 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      n_kv_heads <= 0 || n_kv_heads > pkv::kMaxKvHeads)
+    return PKV_ERR_SHAPE;
+  if (!aligned16(k_codes) || !aligned16(v_codes) || !aligned16(k_scales) ||
+      !aligned16(v_scales) || !aligned16(k_new) || !aligned16(v_new))
+    return PKV_ERR_ALIGN;
+  pkv::QuantAppendArgs a;
+  a.k_codes = static_cast<char*>(k_codes);
+  a.v_codes = static_cast<char*>(v_codes);
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.k_new = static_cast<const char*>(k_new);
+  a.v_new = static_cast<const char*>(v_new);
+  a.block_tables = block_tables;
+  a.positions = positions;
+  a.num_seqs = num_seqs;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.n_kv_heads = n_kv_heads;
+  a.d_head = d_head;
+  a.dtype = dtype;
+  a.kv_format = kv_format;
+  return pkv::launch_append_quantized(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int32_t pkv_paged_decode_attention_quantized(
+    void* out, const void* q, const void* k_codes, const void* v_codes, const float* k_scales,
+    const float* v_scales, const int32_t* block_tables, const int32_t* context_lens,
+    int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+    int32_t block_size, int32_t n_heads, int32_t n_kv_heads, int32_t d_head, float scale,
+    int32_t partition_tokens, int32_t dtype, int32_t kv_format, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (kv_format != PKV_KV_INT8 && kv_format != PKV_KV_FP8) return PKV_ERR_DTYPE;
+  return decode_impl(out, q, k_codes, v_codes, block_tables, context_lens, num_seqs, 1,
+                     max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
+                     n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
+                     workspace_bytes, stream, kv_format, k_scales, v_scales);
 }
 
 int32_t pkv_gather_kv(void* k_out, void* v_out, const void* k_pool, const void* v_pool,

@@ -160,8 +160,10 @@ struct WaveState {
   float o[G][Geo<DT, D>::kEPL] = {};   // lane-partial O[h][chunk c] for its row's tokens
 };
 
-// One 16-token block starting at token blk_tok0; tokens >= tok_end are masked.
-template <int DT, int D, int G>
+// One 16-token block starting at token blk_tok0; tokens >= tok_end are masked. PARTIAL:
+// the block holds such tokens (only the last block of a sequence can); full blocks are
+// compiled without the masking.
+template <int DT, int D, int G, bool PARTIAL>
 __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Tile<DT, D>& t,
                                               const u32x4 (&qf)[Geo<DT, D>::kNK], int blk_tok0,
                                               int tok_end, float scale_log2, int r) {
@@ -182,8 +184,7 @@ __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Til
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(t.k[kk][s]), as_f(qf[kk][s]), acc, 0, 0, 0);
     }
   }
-  // Only the last block of a sequence can be partial (partitions are block aligned).
-  const bool partial = blk_tok0 + kBlockTokens > tok_end;
+  constexpr bool partial = PARTIAL;
   const int tok0 = blk_tok0 + 4 * r;
   float s[4];
   if (partial) {
@@ -205,12 +206,15 @@ __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Til
   st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
   st.m = m_new;
 
-  static_for<G>([&](auto hc) {
-    constexpr int h = decltype(hc)::value;
-    const float a = row_bcast<h>(alpha);
+  // once the maxima settle, alpha is exactly 1 in every column: skip the identity rescale
+  if (__any(alpha != 1.0f)) {
+    static_for<G>([&](auto hc) {
+      constexpr int h = decltype(hc)::value;
+      const float a = row_bcast<h>(alpha);
 #pragma unroll
-    for (int e = 0; e < G_::kEPL; ++e) st.o[h][e] *= a;
-  });
+      for (int e = 0; e < G_::kEPL; ++e) st.o[h][e] *= a;
+    });
+  }
 
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
@@ -262,38 +266,29 @@ __device__ __forceinline__ void store_row_chunk(void* base, size_t idx, const fl
   }
 }
 
-// Stream blocks [blk_begin, blk_begin + n_my) of sequence b, KV head j through one wave:
-// table entries are preloaded 64 at a time into a VGPR, K/V of the next kDepth blocks are
-// in flight while `process(tile, first_token_of_block)` runs on the current one. bad is set
-// if a table entry is outside the pool (the data of that block is then not read).
-template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, typename F>
-__device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
-                                              int n_my, int lane, int& bad, F&& process) {
-  using G_ = Geo<DT, D>;
-  const int r = lane >> 4, c = lane & 15;
-  const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;    // bytes between tokens
-  const size_t blk_stride = (size_t)tok_stride * kBlockTokens;
-  const uint32_t head_off = (uint32_t)j * G_::kRow;
-  const uint32_t k_lane = head_off + c * tok_stride + 16 * r;
-  const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
+// Stream blocks [blk_begin, blk_begin + n_my) of sequence b through one wave: table
+// entries are preloaded 64 at a time into a VGPR, the tiles of the next kDepth blocks are in
+// flight (`load(tile, physical_block)`) while `process(tile, first_token_of_block)` runs on
+// the current one. bad is set if a table entry is outside the pool (that block's data is
+// then not read).
+template <typename TileT, int kDepth, typename L, typename F>
+__device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk_begin, int n_my,
+                                             int lane, int& bad, L&& load, F&& process) {
   const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_begin;
-
   int tbl = 0;   // lane i holds the table entry of block (chunk * 64 + i) of the range
   auto load_table = [&](int first) {
     const int i = first + lane;
     tbl = i < n_my ? trow[i] : 0;
   };
-  auto fetch = [&](Tile<DT, D>& t, int i) {
+  auto fetch = [&](TileT& t, int i) {
     int pb = __builtin_amdgcn_readlane(tbl, i & 63);
     const bool ok = (unsigned)pb < (unsigned)a.num_blocks;
     bad |= !ok;
-    pb = ok ? pb : 0;
-    load_tile<DT, D>(t, a.k_pool + (size_t)pb * blk_stride, a.v_pool + (size_t)pb * blk_stride,
-                     k_lane, v_lane, tok_stride);
+    load(t, ok ? pb : 0);
   };
 
   constexpr int NB = kDepth + 1;
-  Tile<DT, D> tt[NB];
+  TileT tt[NB];
   load_table(0);
 #pragma unroll
   for (int d0 = 0; d0 < kDepth; ++d0)
@@ -310,6 +305,26 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
       process(tt[u], (blk_begin + i) * kBlockTokens);
     }
   }
+}
+
+// stream_tiles over the K/V pools of KV head j in the storage dtype.
+template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, typename F>
+__device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
+                                              int n_my, int lane, int& bad, F&& process) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;    // bytes between tokens
+  const size_t blk_stride = (size_t)tok_stride * kBlockTokens;
+  const uint32_t head_off = (uint32_t)j * G_::kRow;
+  const uint32_t k_lane = head_off + c * tok_stride + 16 * r;
+  const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
+  stream_tiles<Tile<DT, D>, kDepth>(
+      a, b, blk_begin, n_my, lane, bad,
+      [&](Tile<DT, D>& t, int pb) {
+        load_tile<DT, D>(t, a.k_pool + (size_t)pb * blk_stride, a.v_pool + (size_t)pb * blk_stride,
+                         k_lane, v_lane, tok_stride);
+      },
+      process);
 }
 
 // Query fragments (MFMA B operand) for lane column c: 16-byte slices at 64*kk + 16*r of
@@ -336,7 +351,11 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
   u32x4 qf[Geo<DT, D>::kNK];
   load_query<DT, D>(a, c < G, (size_t)b * a.n_heads + (size_t)j * G + c, r, qf);
   stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
-    process_block<DT, D, G>(st, t, qf, tok0, tok_end, a.scale_log2, r);
+    // only the last block of a sequence can be partial (partitions are block aligned)
+    if (tok0 + kBlockTokens > tok_end)
+      process_block<DT, D, G, true>(st, t, qf, tok0, tok_end, a.scale_log2, r);
+    else
+      process_block<DT, D, G, false>(st, t, qf, tok0, tok_end, a.scale_log2, r);
   });
 }
 
@@ -401,8 +420,10 @@ __device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<
   float p[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) p[i] = exp2_fast(s[i] - m_use);
+  if (__any(alpha != 1.0f)) {                 // skip the identity rescale
 #pragma unroll
-  for (int e = 0; e < G_::kEPL; ++e) st.o[e] *= alpha;
+    for (int e = 0; e < G_::kEPL; ++e) st.o[e] *= alpha;
+  }
   const bool tail = blk_tok0 + kBlockTokens > tok_end;
   if constexpr (DT == 0) {
     st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
@@ -537,6 +558,284 @@ __device__ __forceinline__ void write_record_mq(const DecodeArgs& a, const MqSta
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Quantized caches ("LLM 推理优化全景实战" §4.1 affine quantization; "Scaling Book 第 11 章"
+// FP8 / INT8): K and V hold one 8-bit code per element and one (s, z) pair per token and
+// KV head, x^ = s * (Q - z) (FP8: Q is the E4M3 value, z = 0). q and out stay 16-bit.
+// Per block, lane (r, c) holds
+//   * K codes of token c, elements (D/4) r .. (D/4) r + D/4 - 1. Each code converts
+//     exactly to the 16-bit type, so the MFMA contracts q with the raw codes, the query
+//     fragments using the same element mapping d = (D/4) r + 8 kk + i; the score of token
+//     t is then s_t (q.Q_t - z_t sum(q)), the zero point entering once per token;
+//   * V codes of tokens 4r .. 4r + 3, elements EPL c .. EPL c + EPL - 1, dequantized in
+//     fp32 and rounded to the 16-bit type as the A operand of the P.V MFMA (the
+//     multi-query layout with C = G columns);
+//   * (s, z) of K and of V for tokens 4r .. 4r + 3.
+// ---------------------------------------------------------------------------------------
+
+template <int D>
+struct QGeo {
+  static constexpr int kNK = D / 64;           // 16-byte K code loads per lane per block
+  static constexpr int kEPL = D / 16;          // V codes per lane per token
+  static constexpr int kVW = kEPL / 4;         // V code words per lane per token
+};
+
+template <int D>
+struct QTile {
+  u32x4 k[QGeo<D>::kNK];
+  unsigned v[4][QGeo<D>::kVW];
+  f32x4 ks[2];                                 // K (s, z) of tokens 4r .. 4r + 3
+  f32x4 vs[2];                                 // V (s, z) of tokens 4r .. 4r + 3
+};
+
+// Two codes (bytes 2H, 2H + 1 of w) as fp32, exactly.
+template <int FMT, int H>
+__device__ __forceinline__ void codes_to_f32(unsigned w, float& x0, float& x1) {
+  if constexpr (FMT == kKvInt8) {
+    x0 = (float)((w >> (16 * H)) & 0xFFu);
+    x1 = (float)((w >> (16 * H + 8)) & 0xFFu);
+  } else {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, H != 0);   // OCP E4M3 on gfx950
+    x0 = f[0];
+    x1 = f[1];
+  }
+}
+
+// Two fp32 values rounded (to nearest even) into one word of the 16-bit type DT.
+template <int DT>
+__device__ __forceinline__ unsigned pack16(float x0, float x1) {
+  if constexpr (DT == 2) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 h = {(__bf16)x0, (__bf16)x1};
+    return __builtin_bit_cast(unsigned, h);
+  } else {
+    const f16x2 h = {(_Float16)x0, (_Float16)x1};
+    return __builtin_bit_cast(unsigned, h);
+  }
+}
+
+// x rounded (to nearest even) to the 16-bit type DT, returned as fp32.
+template <int DT>
+__device__ __forceinline__ float round16(float x) {
+  if constexpr (DT == 2)
+    return (float)(__bf16)x;
+  else
+    return (float)(_Float16)x;
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma32(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (DT == 2)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(const u32x2& a, const u32x2& b, const f32x4& c) {
+  if constexpr (DT == 2) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                     __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+  } else {
+    typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  }
+}
+
+// Query fragments for the code mapping d = (D/4) r + 8 kk + i, and sum(q) of column c.
+template <int DT, int D>
+__device__ __forceinline__ void load_query_q(const DecodeArgs& a, bool used, size_t row, int r,
+                                             u32x4 (&qf)[D / 32], float& sumq) {
+  const char* qrow = static_cast<const char*>(a.q) + (used ? row : 0) * (D * 2);
+  float sum = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    qf[kk] = used ? *reinterpret_cast<const u32x4*>(qrow + 2 * ((D / 4) * r + 8 * kk)) : z;
+    unsigned w[4] = {qf[kk][0], qf[kk][1], qf[kk][2], qf[kk][3]};
+    float x[8];
+    widen<DT, 4>(w, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sum += x[i];
+  }
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  sumq = sum;
+}
+
+// Running state of a quantized-cache wave: the multi-query state plus, for INT8 codes
+// with bf16 weights, the lane-partial zero-point term sum_t w_t z_t of column c.
+template <int DT, int D>
+struct QState : MqState<DT, D> {
+  float corr = 0.f;
+};
+
+template <int DT, int D, int FMT>
+__device__ __forceinline__ void process_block_q(QState<DT, D>& st, const QTile<D>& t,
+                                                const u32x4 (&qf)[D / 32], float sumq,
+                                                int blk_tok0, int tok_end, float scale_log2,
+                                                int r) {
+  constexpr int EPL = QGeo<D>::kEPL;
+  constexpr int VW = QGeo<D>::kVW;
+  // q . Q_t over the raw codes: kk-th group of 8 codes is bytes 8 kk .. 8 kk + 7 of this
+  // lane's K chunk.
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    const unsigned w0 = t.k[kk >> 1][(kk & 1) * 2], w1 = t.k[kk >> 1][(kk & 1) * 2 + 1];
+    float x[8];
+    codes_to_f32<FMT, 0>(w0, x[0], x[1]);
+    codes_to_f32<FMT, 1>(w0, x[2], x[3]);
+    codes_to_f32<FMT, 0>(w1, x[4], x[5]);
+    codes_to_f32<FMT, 1>(w1, x[6], x[7]);
+    const u32x4 a16 = {pack16<DT>(x[0], x[1]), pack16<DT>(x[2], x[3]), pack16<DT>(x[4], x[5]),
+                       pack16<DT>(x[6], x[7])};
+    acc = mfma32<DT>(a16, qf[kk], acc);
+  }
+  const float sk[4] = {t.ks[0][0], t.ks[0][2], t.ks[1][0], t.ks[1][2]};
+  const float zk[4] = {t.ks[0][1], t.ks[0][3], t.ks[1][1], t.ks[1][3]};
+  const bool tail = blk_tok0 + kBlockTokens > tok_end;
+  const int tok0 = blk_tok0 + 4 * r;
+  float s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float dot = FMT == kKvInt8 ? fmaf(-zk[i], sumq, acc[i]) : acc[i];
+    s[i] = dot * (sk[i] * scale_log2);
+    if (tail) s[i] = tok0 + i < tok_end ? s[i] : -INFINITY;   // unused slots: NaN scales
+  }
+  float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+  bm = fmaxf(bm, __shfl_xor(bm, 16));
+  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  const float m_new = fmaxf(st.m, bm);            // finite: every block has a valid token
+  const float alpha = exp2_fast(st.m - m_new);
+  st.m = m_new;
+  if (__any(alpha != 1.0f)) {                     // skip the identity rescale
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.o[e] *= alpha;
+  }
+  float sv[4] = {t.vs[0][0], t.vs[0][2], t.vs[1][0], t.vs[1][2]};
+  float zv[4] = {t.vs[0][1], t.vs[0][3], t.vs[1][1], t.vs[1][3]};
+  if (tail) {                                     // unused slots hold NaN scales
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = tok0 + i < tok_end ? sv[i] : 0.f;
+      zv[i] = tok0 + i < tok_end ? zv[i] : 0.f;
+    }
+  }
+
+  if constexpr (DT == 2) {
+    // bf16: the V scale joins the weight, w_t = p_t s_t (bf16's exponent range holds any
+    // product), the raw codes are the A operand (exact in bf16), and the zero point leaves
+    // the sum as one term per token: O = sum_t w_t Q_t - sum_t w_t z_t.
+    float p[4], w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = exp2_fast(s[i] - m_new);
+      w[i] = round16<DT>(p[i] * sv[i]);
+    }
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    if constexpr (FMT == kKvInt8)
+      st.corr = st.corr * alpha + ((w[0] * zv[0] + w[1] * zv[1]) + (w[2] * zv[2] + w[3] * zv[3]));
+    const u32x2 wb = {pack16<DT>(w[0], w[1]), pack16<DT>(w[2], w[3])};   // exact
+    unsigned vw[4][VW];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int x = 0; x < VW; ++x)            // codes of unused slots may decode to NaN
+        vw[jj][x] = (!tail || tok0 + jj < tok_end) ? t.v[jj][x] : 0u;
+    float c[4][EPL];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int x = 0; x < VW; ++x) {
+        codes_to_f32<FMT, 0>(vw[jj][x], c[jj][4 * x], c[jj][4 * x + 1]);
+        codes_to_f32<FMT, 1>(vw[jj][x], c[jj][4 * x + 2], c[jj][4 * x + 3]);
+      }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const u32x2 va = {pack16<DT>(c[0][e], c[1][e]), pack16<DT>(c[2][e], c[3][e])};
+      st.o[e] = mfma16<DT>(va, wb, st.o[e]);
+    }
+  } else {
+    // f16: the weights are rounded alone (an f16 product p s could fall below f16's range)
+    // and the V rows are dequantized in fp32, then rounded to f16 as the A operand.
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = round16<DT>(exp2_fast(s[i] - m_new));
+    const u32x2 pb = {pack16<DT>(pr[0], pr[1]), pack16<DT>(pr[2], pr[3])};   // exact
+    st.l = st.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    float xv[4][EPL];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const bool valid = !tail || tok0 + jj < tok_end;
+      const float bias = FMT == kKvInt8 ? -sv[jj] * zv[jj] : 0.f;
+#pragma unroll
+      for (int x = 0; x < VW; ++x) {
+        float cc[4];
+        codes_to_f32<FMT, 0>(t.v[jj][x], cc[0], cc[1]);
+        codes_to_f32<FMT, 1>(t.v[jj][x], cc[2], cc[3]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[jj][4 * x + i] = valid ? fmaf(sv[jj], cc[i], bias) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const u32x2 va = {pack16<DT>(xv[0][e], xv[1][e]), pack16<DT>(xv[2][e], xv[3][e])};
+      st.o[e] = mfma16<DT>(va, pb, st.o[e]);
+    }
+  }
+}
+
+template <int DT, int D, int G, int FMT>
+__device__ __forceinline__ void attend_q(QState<DT, D>& st, int& bad, const DecodeArgs& a,
+                                         int b, int j, int blk_begin, int n_my, int tok_end,
+                                         int lane) {
+  const int r = lane >> 4, c = lane & 15;
+  u32x4 qf[D / 32];
+  float sumq;
+  load_query_q<DT, D>(a, c < G, (size_t)b * a.n_heads + (size_t)j * G + c, r, qf, sumq);
+  const uint32_t tok_stride = (uint32_t)a.n_kv_heads * D;           // code bytes per token
+  const size_t blk_stride = (size_t)tok_stride * kBlockTokens;
+  const uint32_t head_off = (uint32_t)j * D;
+  const uint32_t k_lane = head_off + c * tok_stride + (D / 4) * r;
+  const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * QGeo<D>::kEPL;
+  const char* kc = static_cast<const char*>(a.k_pool);
+  const char* vc = static_cast<const char*>(a.v_pool);
+  stream_tiles<QTile<D>, 2>(
+      a, b, blk_begin, n_my, lane, bad,
+      [&](QTile<D>& t, int pb) {
+        const char* kb = kc + (size_t)pb * blk_stride;
+        const char* vb = vc + (size_t)pb * blk_stride;
+#pragma unroll
+        for (int x = 0; x < QGeo<D>::kNK; ++x)
+          t.k[x] = *reinterpret_cast<const u32x4*>(kb + (k_lane + 16u * x));
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const char* src = vb + (v_lane + jj * tok_stride);
+          if constexpr (QGeo<D>::kVW == 2) {
+            const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+            t.v[jj][0] = w[0];
+            t.v[jj][1] = w[1];
+          } else {
+            t.v[jj][0] = __builtin_nontemporal_load(reinterpret_cast<const unsigned*>(src));
+          }
+        }
+        const size_t srow = (((size_t)pb * a.n_kv_heads + j) * kBlockTokens + 4 * r) * 2;
+        t.ks[0] = *reinterpret_cast<const f32x4*>(a.k_scales + srow);
+        t.ks[1] = *reinterpret_cast<const f32x4*>(a.k_scales + srow + 4);
+        t.vs[0] = *reinterpret_cast<const f32x4*>(a.v_scales + srow);
+        t.vs[1] = *reinterpret_cast<const f32x4*>(a.v_scales + srow + 4);
+      },
+      [&](const QTile<D>& t, int tok0) {
+        process_block_q<DT, D, FMT>(st, t, qf, sumq, tok0, tok_end, a.scale_log2, r);
+      });
+}
+
 // Sum the lane-partial l and O over the four rows: afterwards every lane holds l of
 // head c, and lane (r, c) holds O[h][chunk c] for every head h.
 template <int DT, int D, int G>
@@ -608,12 +907,28 @@ __device__ __forceinline__ void write_nan_rows(const DecodeArgs& a, size_t row0,
 
 // A whole-sequence-or-segment of one wave: attend over blocks [blk_begin, +n_my) of
 // sequence b for KV head j, then write the outputs (whole) or the records rec(column).
-template <int DT, int D, int G, bool MQ, typename R>
+template <int DT, int D, int G, int MODE, typename R>
 __device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, int blk_begin,
                                             int n_my, int tok_end, int n_ctx, bool whole,
                                             int lane, R&& rec) {
   int bad = 0;
-  if constexpr (!MQ) {
+  if constexpr (MODE == kModeQuantInt8 || MODE == kModeQuantFp8) {
+    QState<DT, D> st;
+    attend_q<DT, D, G, MODE == kModeQuantInt8 ? kKvInt8 : kKvFp8>(st, bad, a, b, j, blk_begin,
+                                                                n_my, tok_end, lane);
+    st.l += __shfl_xor(st.l, 16);
+    st.l += __shfl_xor(st.l, 32);
+    if constexpr (MODE == kModeQuantInt8 && DT == 2) {     // O -= sum_t w_t z_t (column c)
+      st.corr += __shfl_xor(st.corr, 16);
+      st.corr += __shfl_xor(st.corr, 32);
+#pragma unroll
+      for (int e = 0; e < Geo<DT, D>::kEPL; ++e) st.o[e] -= st.corr;
+    }
+    if (whole)
+      write_final_mq<DT, D, G>(a, st, bad, b, j, lane);
+    else
+      write_record_mq<DT, D, G>(a, st, bad, lane, rec);
+  } else if constexpr (MODE == kModeSingle) {
     WaveState<DT, D, G> st;
     attend<DT, D, G>(st, bad, a, b, j, blk_begin, n_my, tok_end, lane);
     finish_rows<DT, D, G>(st);
@@ -656,7 +971,7 @@ __device__ __forceinline__ bool usable(const DecodeArgs& a, int b, int n_ctx) {
 
 // Fixed partitions: workgroup = NW waves = KV heads hg*NW .. hg*NW+NW-1 of one
 // (partition, sequence); grid (head groups, partitions, sequences).
-template <int DT, int D, int G, int NW, bool MQ>
+template <int DT, int D, int G, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
   const int hg = blockIdx.x, p = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -676,7 +991,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
   const int tok_end = min(n_ctx, (p + 1) * P);
   const int blk_begin = (p * P) >> 4;
   const int n_my = ((tok_end + 15) >> 4) - blk_begin;     // >= 1
-  run_segment<DT, D, G, MQ>(a, b, j, blk_begin, n_my, tok_end, n_ctx, n_part == 1, lane,
+  run_segment<DT, D, G, MODE>(a, b, j, blk_begin, n_my, tok_end, n_ctx, n_part == 1, lane,
                             [&](int c) { return mq_row<G>(a, b, j, c) * a.max_partitions + p; });
 }
 
@@ -688,7 +1003,7 @@ __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
 // a record for merge_kernel. Segments of stream s = hg * num_seqs + b are produced by
 // consecutive workgroups in increasing order of w, so (w + s) names each segment
 // uniquely: the record of its column c (of C = G * q_len) is ((w + s) * NW + wave) * C + c.
-template <int DT, int D, int G, int NW, bool MQ>
+template <int DT, int D, int G, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW;
   __shared__ int sm_pref[kSplitMaxSeqs + 1];   // blocks of sequences before b
@@ -754,7 +1069,7 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
       const int tok_end = min(n_ctx, (skip + blk0 + n_my) * kBlockTokens);
       const size_t rec0 = ((size_t)(w + (long long)hg * B + b) * NW + wave) * C;
       // a sequence with a shared prefix always leaves a record: the merge adds the prefix
-      run_segment<DT, D, G, MQ>(a, b, j, skip + blk0, n_my, tok_end, n_ctx,
+      run_segment<DT, D, G, MODE>(a, b, j, skip + blk0, n_my, tok_end, n_ctx,
                                 skip == 0 && blk0 == 0 && n_my == nb && !(a.seq_group && a.seq_group[b] >= 0),
                                 lane, [&](int c) { return rec0 + c; });
     }
@@ -1003,17 +1318,17 @@ int resident_workgroups(K kernel, int threads) {
   return per_cu * cus;
 }
 
-template <int DT, int D, int G, int NW, bool MQ>
+template <int DT, int D, int G, int NW, int MODE>
 hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
   bool need_merge;
   if (a.split) {
-    auto kernel = decode_split_kernel<DT, D, G, NW, MQ>;
+    auto kernel = decode_split_kernel<DT, D, G, NW, MODE>;
     a.split_workgroups = min(kSplitMaxWorkgroups, resident_workgroups(kernel, 64 * NW));
     hipLaunchKernelGGL(kernel, dim3(a.split_workgroups), dim3(64 * NW), 0, stream, a);
     need_merge = true;
   } else {
     const dim3 grid((a.n_kv_heads + NW - 1) / NW, a.max_partitions, a.num_seqs);
-    hipLaunchKernelGGL((decode_fixed_kernel<DT, D, G, NW, MQ>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((decode_fixed_kernel<DT, D, G, NW, MODE>), grid, dim3(64 * NW), 0, stream, a);
     need_merge = a.max_partitions > 1;
   }
   hipError_t e = hipGetLastError();
@@ -1025,8 +1340,8 @@ hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
 
 template <int DT, int D, int G, int NW>
 hipError_t launch_mq(const DecodeArgs& a, hipStream_t stream) {
-  if (a.q_len == 1) return launch_typed<DT, D, G, NW, false>(a, stream);
-  return launch_typed<DT, D, G, NW, true>(a, stream);
+  if (a.q_len == 1) return launch_typed<DT, D, G, NW, kModeSingle>(a, stream);
+  return launch_typed<DT, D, G, NW, kModeMulti>(a, stream);
 }
 
 template <int DT, int D, int G>
@@ -1054,6 +1369,36 @@ template <int DT>
 hipError_t launch_dim(const DecodeArgs& a, int d_head, int group, hipStream_t stream) {
   if (d_head == 64) return launch_group<DT, 64>(a, group, stream);
   if (d_head == 128) return launch_group<DT, 128>(a, group, stream);
+  return hipErrorInvalidValue;
+}
+
+template <int DT, int D, int G>
+hipError_t launch_quant_group(const DecodeArgs& a, int fmt, hipStream_t stream) {
+  // eight KV heads per workgroup when they divide evenly (every variant fits 256 registers)
+  if (max_waves_per_workgroup(a.n_kv_heads) == 8) {
+    if (fmt == kKvInt8) return launch_typed<DT, D, G, 8, kModeQuantInt8>(a, stream);
+    return launch_typed<DT, D, G, 8, kModeQuantFp8>(a, stream);
+  }
+  if (fmt == kKvInt8) return launch_typed<DT, D, G, 4, kModeQuantInt8>(a, stream);
+  return launch_typed<DT, D, G, 4, kModeQuantFp8>(a, stream);
+}
+
+template <int DT, int D>
+hipError_t launch_quant_dim(const DecodeArgs& a, int fmt, int group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_quant_group<DT, D, 1>(a, fmt, stream);
+    case 2: return launch_quant_group<DT, D, 2>(a, fmt, stream);
+    case 4: return launch_quant_group<DT, D, 4>(a, fmt, stream);
+    case 8: return launch_quant_group<DT, D, 8>(a, fmt, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_quant_dtype(const DecodeArgs& a, int fmt, int d_head, int group,
+                              hipStream_t stream) {
+  if (d_head == 64) return launch_quant_dim<DT, 64>(a, fmt, group, stream);
+  if (d_head == 128) return launch_quant_dim<DT, 128>(a, fmt, group, stream);
   return hipErrorInvalidValue;
 }
 
@@ -1094,6 +1439,14 @@ hipError_t launch_shared_prefix(const DecodeArgs& a, int dtype, int d_head, int 
     case 2: return launch_prefix_dim<2>(a, d_head, group, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_decode_quantized(const DecodeArgs& a, int dtype, int kv_format, int d_head,
+                                   int group, hipStream_t stream) {
+  if (kv_format != kKvInt8 && kv_format != kKvFp8) return hipErrorInvalidValue;
+  if (dtype == 1) return launch_quant_dtype<1>(a, kv_format, d_head, group, stream);
+  if (dtype == 2) return launch_quant_dtype<2>(a, kv_format, d_head, group, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d_head, int group, hipStream_t stream) {

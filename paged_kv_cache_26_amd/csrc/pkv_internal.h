@@ -17,6 +17,14 @@ constexpr int kPrefixPartition = 512;     // tokens per prefix-pass partition
 constexpr int kPrefixWaves = 4;           // prefix-pass waves per workgroup, 16 columns each
 constexpr int kPrefixColumns = 16 * kPrefixWaves;
 
+// Quantized KV formats (values of the C ABI's kv_format) and the decode kernels' modes.
+constexpr int kKvInt8 = 1;
+constexpr int kKvFp8 = 2;
+constexpr int kModeSingle = 0;      // one query per sequence, P.V on the vector ALU
+constexpr int kModeMulti = 1;       // q_len queries per sequence, P.V on the matrix cores
+constexpr int kModeQuantInt8 = 2;   // one query, INT8 codes + (s, z) per token and KV head
+constexpr int kModeQuantFp8 = 3;    // one query, E4M3 codes + (s, 0) per token and KV head
+
 // Waves per decode workgroup (one KV head each) used with this many KV heads. The
 // launcher may use fewer (4) for kernels that do not fit 256 registers per lane; this is
 // the upper bound the workspace is sized for.
@@ -78,14 +86,37 @@ struct DecodeArgs {
                                      // disagrees with the group's in partition p, or the
                                      // group has more than max_group_size members
   float scale_log2;                  // scale * log2(e): scores are kept in base 2
+  // Quantized caches: k_pool / v_pool hold 8-bit codes and these the (s, z) pairs,
+  // [num_blocks][n_kv_heads][16][2] fp32.
+  const float* k_scales;
+  const float* v_scales;
+};
+
+// Quantizing append: one token per sequence, K and V rows of every KV head quantized to
+// 8-bit codes with one (s, z) pair each.
+struct QuantAppendArgs {
+  char* k_codes;
+  char* v_codes;
+  float* k_scales;                   // [num_blocks][n_kv_heads][16][2]
+  float* v_scales;
+  const char* k_new;                 // [num_seqs][n_kv_heads][d_head] in dtype
+  const char* v_new;
+  const int32_t* block_tables;
+  const int32_t* positions;
+  int32_t num_seqs, max_blocks_per_seq, num_blocks, n_kv_heads, d_head;
+  int32_t dtype;                     // of k_new / v_new: 0 f32, 1 f16, 2 bf16
+  int32_t kv_format;                 // kKvInt8 or kKvFp8
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_append_quantized(const QuantAppendArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
 // dtype: 0 f32, 1 f16, 2 bf16; d_head 64/128; group 1/2/4/8 (validated by the caller).
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d_head, int group,
                          hipStream_t stream);
 // Shared-prefix decode (split mode, q_len 1): prefix pass, split pass, merge.
+hipError_t launch_decode_quantized(const DecodeArgs& a, int dtype, int kv_format, int d_head,
+                                   int group, hipStream_t stream);
 hipError_t launch_shared_prefix(const DecodeArgs& a, int dtype, int d_head, int group,
                                 hipStream_t stream);
 

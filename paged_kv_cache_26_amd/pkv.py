@@ -17,6 +17,8 @@ import torch
 from .build import LIB_PATH
 
 PKV_F32, PKV_F16, PKV_BF16 = 0, 1, 2
+PKV_KV_INT8, PKV_KV_FP8 = 1, 2
+KV_FORMAT_CODE = {"int8": PKV_KV_INT8, "fp8": PKV_KV_FP8}
 _DTYPE_CODE = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
 BLOCK_SIZE = 16
 
@@ -66,6 +68,10 @@ _SIGNATURES = {
     "pkv_bm_tables": (_c_i32, [_c_ptr, _c_ptr, _c_i32, _c_i32, _c_ptr]),
     "pkv_copy_blocks": (_c_i32, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                  _c_i32, _c_ptr]),
+    "pkv_kv_append_quantized": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 8 + [_c_ptr]),
+    "pkv_paged_decode_attention_quantized": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 8 +
+                                             [ctypes.c_float, _c_i32, _c_i32, _c_i32, _c_ptr,
+                                              _c_size, _c_ptr]),
     "pkv_find_shared_prefixes": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr,
                                           _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
 }
@@ -277,6 +283,65 @@ def pkv_paged_decode_attention_shared_prefix(out, q, k_pool, v_pool, block_table
         _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_paged_decode_attention_shared_prefix")
+    return out
+
+
+def _kv_format(fmt) -> int:
+    code = KV_FORMAT_CODE.get(fmt, fmt)
+    _require(code in (PKV_KV_INT8, PKV_KV_FP8), "kv_format must be 'int8' or 'fp8'")
+    return int(code)
+
+
+def pkv_kv_append_quantized(k_codes, v_codes, k_scales, v_scales, k_new, v_new, block_tables,
+                            positions, kv_format, stream=None) -> None:
+    """Quantize k_new/v_new [B, H_kv, d] into the uint8 code pools [N, 16, H_kv, d] and the
+    (s, z) pools [N, H_kv, 16, 2] at positions[b] (in place)."""
+    lib = load_library()
+    _check_device(k_codes, v_codes, k_scales, v_scales, k_new, v_new, block_tables, positions)
+    _require(k_codes.dtype == torch.uint8 and v_codes.dtype == torch.uint8, "codes must be uint8")
+    _require(k_scales.dtype == torch.float32 and v_scales.dtype == torch.float32,
+             "scales must be float32")
+    _require(k_new.dtype in _DTYPE_CODE and v_new.dtype == k_new.dtype, "unsupported dtype")
+    _require(k_codes.dim() == 4 and k_codes.shape == v_codes.shape, "codes must be [N, 16, H_kv, d]")
+    N, bs, Hkv, d = k_codes.shape
+    _require(k_scales.shape == (N, Hkv, bs, 2) and v_scales.shape == k_scales.shape,
+             "scales must be [N, H_kv, 16, 2]")
+    _require(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [B, H_kv, d]")
+    st = lib.pkv_kv_append_quantized(
+        _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales), _ptr(k_new), _ptr(v_new),
+        _ptr(block_tables), _ptr(positions), k_new.shape[0], block_tables.shape[1], N, bs, Hkv,
+        d, _DTYPE_CODE[k_new.dtype], _kv_format(kv_format), _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_kv_append_quantized")
+
+
+def pkv_paged_decode_attention_quantized(out, q, k_codes, v_codes, k_scales, v_scales,
+                                         block_tables, context_lens, max_context_len: int,
+                                         kv_format, scale: float | None = None,
+                                         partition_tokens: int = 0, workspace=None,
+                                         stream=None):
+    """pkv_paged_decode_attention over a quantized cache (q/out f16 or bf16). Returns out."""
+    lib = load_library()
+    _check_device(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens)
+    _require(q.dtype in (torch.float16, torch.bfloat16) and out.dtype == q.dtype,
+             "q and out must be f16 or bf16")
+    _require(k_codes.dtype == torch.uint8 and v_codes.dtype == torch.uint8, "codes must be uint8")
+    _require(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, H, d]")
+    B, H, d = q.shape
+    N, bs, Hkv, _ = k_codes.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = pkv_decode_workspace_bytes(B, H, Hkv, d, max_context_len, partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pkv_paged_decode_attention_quantized(
+        _ptr(out), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales),
+        _ptr(block_tables), _ptr(context_lens), B, block_tables.shape[1], N,
+        int(max_context_len), bs, H, Hkv, d, float(scale), int(partition_tokens),
+        _DTYPE_CODE[q.dtype], _kv_format(kv_format), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_paged_decode_attention_quantized")
     return out
 
 

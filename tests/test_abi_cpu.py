@@ -174,3 +174,23 @@ def test_parity_checker_rejects_negative_controls():
     rounded16 = ref.astype(np.float16).astype(np.float64)
     assert within(rounded16, ref, "f16")[0]
     assert within(ref.astype(np.float32).astype(np.float64), ref, "f32")[0]
+
+
+def test_quantized_entry_points_reject_bad_arguments_on_host(lib):
+    f = lib.pkv_kv_append_quantized
+    good = [0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 0x600000, 0x700000, 0x800000,
+            4, 8, 64, 16, 8, 128, 2, 1, None]
+    for idx, val, code in [(0, 0, -1), (2, 0, -1), (14, 5, -3), (15, 0, -3), (15, 3, -3),
+                           (11, 32, -5), (13, 96, -4), (12, 300, -2), (3, 0x400004, -11)]:
+        args = list(good)
+        args[idx] = val
+        assert f(*args) == code, (idx, val)
+    g = lib.pkv_paged_decode_attention_quantized
+    good = [0x1000000, 0x2000000, 0x10000000, 0x20000000, 0x300000, 0x400000, 0x30000, 0x40000,
+            4, 64, 64, 700, 16, 32, 8, 128, 0.1, 0, 2, 1, 0, 0, None]
+    for idx, val, code in [(19, 0, -3), (19, 3, -3), (18, 0, -3), (4, 0, -1), (5, 0, -1),
+                           (15, 96, -4), (13, 24, -6), (4, 0x300008, -11), (11, 0, -7)]:
+        args = list(good)
+        args[idx] = val
+        assert g(*args) == code, (idx, val)
+    assert g(*good) == -9                     # the balanced split needs its workspace

@@ -265,3 +265,9 @@ def test_planted_zero_point_sign_error_is_caught(monkeypatch):
     got = orc.paged_decode_attention_quantized(wl.q, kc, vc, ks, vs, wl.block_tables,
                                                wl.context_lens, 16, wl.scale, "int8", wl.dtype)
     assert not within(got, ref, "bf16")[0]
+
+
+def test_int8_zero_point_is_positive_zero():
+    """A row without negative values has lo = 0 and z = 0, stored as +0 (bit pattern 0)."""
+    _, s, z = orc.quantize_row(np.float32([0.5, 1.0, 2.0]), "int8")
+    assert np.float32(z).view(np.uint32) == 0
