@@ -37,7 +37,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 # (workload id, partition_tokens). Each entry records the sha256 prefix of the decode kernel
 # source it was measured on; it is reported only while that source is unchanged.
 MEASURED_TRAFFIC = {
-    (2, 0): {"bytes": 1193217955, "decode_source_sha256": "0ef28e6feea7663d"},
+    (2, 0): {"bytes": 1193268269, "decode_source_sha256": "0a62aded8d9a1841"},
 }
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", "pkv_decode.hip")
 

@@ -126,7 +126,17 @@ struct Tile {
 // lives in scalar registers); k_lane / v_lane: this lane's byte offsets inside the block,
 // which fit 32 bits (a block is at most 16 * 256 * 128 * 4 bytes), so each load is the
 // scalar-base + 32-bit-offset form and needs no 64-bit address arithmetic per lane.
-template <int DT, int D>
+// V loads carry the non-temporal hint when each V byte is used once (NT_V); the shared-
+// prefix pass, whose four waves read the same blocks, keeps them cacheable.
+template <typename T, bool NT>
+__device__ __forceinline__ T load_v(const char* p) {
+  if constexpr (NT)
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+  else
+    return *reinterpret_cast<const T*>(p);
+}
+
+template <int DT, int D, bool NT_V = true>
 __device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kblk, const char* vblk,
                                           uint32_t k_lane, uint32_t v_lane, uint32_t tok_stride) {
   using G_ = Geo<DT, D>;
@@ -137,16 +147,16 @@ __device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kblk, cons
   for (int jj = 0; jj < 4; ++jj) {
     const char* src = vblk + (v_lane + jj * tok_stride);
     if constexpr (G_::kVW == 8) {
-      const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
-      const u32x4 a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src) + 1);
+      const u32x4 a0 = load_v<u32x4, NT_V>(src);
+      const u32x4 a1 = load_v<u32x4, NT_V>(src + 16);
 #pragma unroll
       for (int x = 0; x < 4; ++x) { t.v[jj][x] = a0[x]; t.v[jj][4 + x] = a1[x]; }
     } else if constexpr (G_::kVW == 4) {
-      const u32x4 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+      const u32x4 a0 = load_v<u32x4, NT_V>(src);
 #pragma unroll
       for (int x = 0; x < 4; ++x) t.v[jj][x] = a0[x];
     } else {
-      const u32x2 a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(src));
+      const u32x2 a0 = load_v<u32x2, NT_V>(src);
       t.v[jj][0] = a0[0];
       t.v[jj][1] = a0[1];
     }
@@ -308,7 +318,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
 }
 
 // stream_tiles over the K/V pools of KV head j in the storage dtype.
-template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, typename F>
+template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true, typename F>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
                                               int n_my, int lane, int& bad, F&& process) {
   using G_ = Geo<DT, D>;
@@ -321,8 +331,8 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
   stream_tiles<Tile<DT, D>, kDepth>(
       a, b, blk_begin, n_my, lane, bad,
       [&](Tile<DT, D>& t, int pb) {
-        load_tile<DT, D>(t, a.k_pool + (size_t)pb * blk_stride, a.v_pool + (size_t)pb * blk_stride,
-                         k_lane, v_lane, tok_stride);
+        load_tile<DT, D, NT_V>(t, a.k_pool + (size_t)pb * blk_stride,
+                               a.v_pool + (size_t)pb * blk_stride, k_lane, v_lane, tok_stride);
       },
       process);
 }
@@ -1276,7 +1286,8 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeArgs a) {
   int bad = 0;
   // The four waves read the same blocks, so each keeps more of them in flight than a
   // decode wave does.
-  stream_blocks<DT, D, kPrefixDepth<DT, D>>(a, leader, j, blk_begin, blk_end - blk_begin, lane, bad,
+  stream_blocks<DT, D, kPrefixDepth<DT, D>, false>(a, leader, j, blk_begin, blk_end - blk_begin,
+                                                   lane, bad,
                                             [&](const Tile<DT, D>& tl, int tok0) {
     process_block_mq<DT, D>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
   });
