@@ -195,6 +195,10 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
             "algorithmic_bytes_per_launch": by["decode"],
         },
     }
+    res["ceiling"] = stream_ceiling(by["kv"], dev)
+    res["ceiling"]["frac_of_ceiling"] = round(achieved / res["ceiling"]["gbps"], 4)
+    if cfg == 5:
+        res["cold"] = cold_steps(step, args, by, dev, stream)
     if args.copy_calibration:
         n = args.copy_calibration << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -215,6 +219,75 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
     return res
 
 
+def stream_ceiling(nbytes: int, dev, reps: int = 10) -> dict:
+    """The achievable read rate: pkv_stream_read over a fresh buffer of nbytes (rounded up
+    to 16), best over a few grid sizes, HIP events on the current stream."""
+    import torch
+
+    from paged_kv_cache_26_amd import pkv
+
+    n = (nbytes + 15) // 16 * 16
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty(cus * 32 * 256, dtype=torch.int32, device=dev)
+    best, best_wg = 0.0, 0
+    for per_cu in (4, 8, 16, 32):
+        wg = cus * per_cu
+        for _ in range(2):
+            pkv.pkv_stream_read(buf, sink, wg)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            pkv.pkv_stream_read(buf, sink, wg)
+        e1.record()
+        torch.cuda.synchronize()
+        gbps = n / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+        if gbps > best:
+            best, best_wg = gbps, wg
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"kind": "streaming read (pkv_stream_read, 16-byte non-temporal loads) of a buffer "
+                    "of the step's KV bytes", "gbps": round(best, 1), "workgroups": best_wg}
+
+
+def cold_steps(step, args, by, dev, stream) -> dict:
+    """The same step with the 256 MB last-level cache (MALL) flushed before each one by
+    writing a 1 GiB scratch buffer outside the timed region (shared blocks then come
+    from HBM every step)."""
+    import torch
+
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for i in range(K):
+        flush.fill_(i & 0xFF)
+        ev[i][0].record(stream)
+        step(ev[i][1])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in ev])
+    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    del flush
+    torch.cuda.empty_cache()
+    dec_s = float(dec_ms.mean()) * 1e-3
+    return {"us_per_step_median": round(float(np.median(step_ms)) * 1e3, 2),
+            "decode_us_mean": round(dec_s * 1e6, 2),
+            "decode_kv_gbps_logical": round(by["kv"] / dec_s / 1e9, 1),
+            "decode_unique_gbps": round(by["kv_unique"] / dec_s / 1e9, 1),
+            "flush": "1 GiB written before each step, outside the timed region"}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(wl, target_s: float) -> dict:
     """The fp64 oracle, unchanged, on a bounded sample: whole sequences in order until the
     time budget is spent; GB/s = KV bytes of those sequences / oracle time."""
@@ -226,9 +299,10 @@ def cpu_baseline(wl, target_s: float) -> dict:
                            wl.positions, 16)
     s = wl.spec
     e = {"f32": 4, "f16": 2, "bf16": 2}[s.dtype]
-    done_bytes, done_seqs, spent = 0, 0, 0.0
-    with threadpool_limits(limits=1):
-        while spent < target_s:
+
+    def passes(budget_s):
+        done_bytes, done_seqs, spent = 0, 0, 0.0
+        while spent < budget_s:
             for b in range(wl.batch):
                 pairs = [(b, h) for h in range(s.n_heads)]
                 t0 = time.perf_counter()
@@ -237,8 +311,15 @@ def cpu_baseline(wl, target_s: float) -> dict:
                 spent += time.perf_counter() - t0
                 done_bytes += int(wl.context_lens[b]) * 2 * s.n_kv_heads * s.d_head * e
                 done_seqs += 1
-                if spent >= target_s:
+                if spent >= budget_s:
                     break
+        return done_bytes, done_seqs, spent
+
+    with threadpool_limits(limits=1):
+        done_bytes, done_seqs, spent = passes(target_s)
+    cpus = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cpus):     # the same oracle with BLAS free to use every core
+        all_bytes, _, all_spent = passes(target_s / 2)
     return {
         "value": round(done_bytes / spent / 1e9, 4),
         "unit": "GB/s",
@@ -246,8 +327,10 @@ def cpu_baseline(wl, target_s: float) -> dict:
         "kind": "oracle",
         "sample": f"{done_seqs} sequence passes (all heads) over the {wl.batch}-sequence "
                   f"batch in order; {done_bytes} KV bytes in {spent:.1f} s",
-        "cpu": platform.processor() or platform.machine(),
-        "host_cpus_available": len(os.sched_getaffinity(0)),
+        "all_cores_value": round(all_bytes / all_spent / 1e9, 4),
+        "all_cores": cpus,
+        "cpu": _cpu_model(),
+        "host_cpus_available": cpus,
     }
 
 

@@ -306,6 +306,17 @@ int32_t pkv_paged_decode_attention_quantized(
     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pkv_stream_read - measurement utility: read `bytes` (a multiple of 16) of the device
+ * buffer `buf` once with 16-byte non-temporal loads, the plain streaming read whose rate
+ * is the achievable HBM ceiling for the decode kernels. Each of the workgroups * 256
+ * threads writes the XOR of the 32-bit words it read to sink[thread] (device, at least
+ * workgroups * 256 words; PKV_ERR_WORKSPACE otherwise). workgroups = 0 picks 8 per
+ * compute unit. Nothing else is written.
+ */
+int32_t pkv_stream_read(const void* buf, size_t bytes, uint32_t* sink, size_t sink_words,
+                        int32_t workgroups, hipStream_t stream);
+
+/*
  * pkv_kv_bytes_per_token - bytes one token occupies in the KV cache of a whole model:
  * 2 * n_layers * n_kv_heads * d_head * dtype_bytes (host only).
  *

@@ -14,7 +14,8 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
-SOURCES = ["pkv_capi.hip", "pkv_append.hip", "pkv_decode.hip", "pkv_block_manager.hip"]
+SOURCES = ["pkv_capi.hip", "pkv_append.hip", "pkv_decode.hip", "pkv_block_manager.hip",
+           "pkv_measure.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled on purpose: every fp32 operation in the kernels

@@ -389,7 +389,9 @@ struct MqState {
 };
 
 // lim: this lane's column sees tokens < lim; lim_min: the smallest lim of the wave.
-template <int DT, int D>
+// PARTIAL: some column sees only part of the block (blk_tok0 + 16 > lim_min); blocks seen
+// whole by every column are compiled without the masking.
+template <int DT, int D, bool PARTIAL>
 __device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<DT, D>& t,
                                                  const u32x4 (&qf)[Geo<DT, D>::kNK], int blk_tok0,
                                                  int tok_end, int lim, int lim_min,
@@ -410,10 +412,10 @@ __device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(as_f(t.k[kk][s]), as_f(qf[kk][s]), acc, 0, 0, 0);
     }
   }
-  const bool partial = blk_tok0 + kBlockTokens > lim_min;
+  constexpr bool partial = PARTIAL;
   const int tok0 = blk_tok0 + 4 * r;
   float s[4];
-  if (partial) {
+  if constexpr (partial) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] = (tok0 + i < lim) ? acc[i] * scale_log2 : -INFINITY;
   } else {
@@ -434,7 +436,7 @@ __device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<
 #pragma unroll
     for (int e = 0; e < G_::kEPL; ++e) st.o[e] *= alpha;
   }
-  const bool tail = blk_tok0 + kBlockTokens > tok_end;
+  const bool tail = partial && blk_tok0 + kBlockTokens > tok_end;   // lim_min <= tok_end
   if constexpr (DT == 0) {
     st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
 #pragma unroll
@@ -521,7 +523,10 @@ __device__ __forceinline__ void attend_mq(MqState<DT, D>& st, int& bad, const De
   const int lim = c < C ? min(tok_end, first_visible_end + c / G) : tok_end;
   const int lim_min = min(tok_end, first_visible_end);
   stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
-    process_block_mq<DT, D>(st, t, qf, tok0, tok_end, lim, lim_min, a.scale_log2, r);
+    if (tok0 + kBlockTokens > lim_min)
+      process_block_mq<DT, D, true>(st, t, qf, tok0, tok_end, lim, lim_min, a.scale_log2, r);
+    else
+      process_block_mq<DT, D, false>(st, t, qf, tok0, tok_end, lim, lim_min, a.scale_log2, r);
   });
 }
 
@@ -1289,7 +1294,10 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeArgs a) {
   stream_blocks<DT, D, kPrefixDepth<DT, D>, false>(a, leader, j, blk_begin, blk_end - blk_begin,
                                                    lane, bad,
                                             [&](const Tile<DT, D>& tl, int tok0) {
-    process_block_mq<DT, D>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
+    if (tok0 + kBlockTokens > tok_end)
+      process_block_mq<DT, D, true>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
+    else
+      process_block_mq<DT, D, false>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
   });
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);

@@ -72,6 +72,7 @@ _SIGNATURES = {
     "pkv_paged_decode_attention_quantized": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 8 +
                                              [ctypes.c_float, _c_i32, _c_i32, _c_i32, _c_ptr,
                                               _c_size, _c_ptr]),
+    "pkv_stream_read": (_c_i32, [_c_ptr, _c_size, _c_ptr, _c_size, _c_i32, _c_ptr]),
     "pkv_find_shared_prefixes": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr,
                                           _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
 }
@@ -343,6 +344,19 @@ def pkv_paged_decode_attention_quantized(out, q, k_codes, v_codes, k_scales, v_s
     if st != 0:
         raise PkvError(st, "pkv_paged_decode_attention_quantized")
     return out
+
+
+def pkv_stream_read(buf, sink, workgroups: int = 0, nbytes: int | None = None,
+                    stream=None) -> None:
+    """Read nbytes (default: all) of the GPU tensor buf once (streaming-read ceiling)."""
+    lib = load_library()
+    _check_device(buf, sink)
+    _require(sink.dtype == torch.int32 or sink.dtype == torch.uint32, "sink must be 32-bit")
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    st = lib.pkv_stream_read(_ptr(buf), n, _ptr(sink), sink.numel(), int(workgroups),
+                             _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_stream_read")
 
 
 def pkv_gather_kv(k_out, v_out, k_pool, v_pool, block_tables, context_lens,

@@ -194,3 +194,12 @@ def test_quantized_entry_points_reject_bad_arguments_on_host(lib):
         args[idx] = val
         assert g(*args) == code, (idx, val)
     assert g(*good) == -9                     # the balanced split needs its workspace
+
+
+def test_stream_read_rejects_bad_arguments_on_host(lib):
+    f = lib.pkv_stream_read
+    assert f(0, 1024, 0x2000, 1 << 20, 4, None) == -1
+    assert f(0x1000, 0, 0x2000, 1 << 20, 4, None) == -2
+    assert f(0x1000, 1000, 0x2000, 1 << 20, 4, None) == -2      # not a multiple of 16
+    assert f(0x1008, 1024, 0x2000, 1 << 20, 4, None) == -11
+    assert f(0x1000, 1024, 0x2000, 1023, 4, None) == -9         # sink shorter than 4 * 256
