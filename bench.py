@@ -701,10 +701,10 @@ def run_quantized(args) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     if os.environ.get("WORLD_SIZE", "1") != "1":
-        print("this build runs on one GPU only", file=sys.stderr)
+        print("the benchmark runs on one GPU only", file=sys.stderr)
         sys.exit(2)
     if args.component == "block-manager":
         print(json.dumps(run_block_manager(args)), flush=True)

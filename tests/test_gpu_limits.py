@@ -1,0 +1,144 @@
+"""Limits of the decode path on the GPU: pools beyond 4 GiB (64-bit block offsets), more
+sequences than the balanced split holds (fixed-partition fallback), the batch size at the
+split mode's limit, a sequence filling its whole table, and KV-head counts that are not a
+multiple of 8 (four-wave workgroups)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import pkv_oracle as orc
+from paged_kv_cache_26_amd import pkv
+from paged_kv_cache_26_amd import workload as wlm
+from tests.parity import assert_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    assert torch.cuda.is_available()
+    pkv.load_library()
+
+
+def _decode(t, wl, ptok=0):
+    out = torch.empty_like(t["q"])
+    pkv.pkv_paged_decode_attention(out, t["q"], t["k_pool"], t["v_pool"], t["block_tables"],
+                                   t["context_lens"], wl.max_context_len, wl.scale,
+                                   partition_tokens=ptok)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+def _oracle(wl, pairs=None):
+    kp, vp = orc.kv_append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.block_tables,
+                           wl.positions, 16)
+    return orc.paged_decode_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                      wl.scale, wl.dtype, pairs=pairs)
+
+
+def _sampled(wl, n, seed):
+    rng = np.random.default_rng(seed)
+    seqs = sorted(set(rng.choice(wl.batch, size=n, replace=False).tolist()) |
+                  {int(np.argmax(wl.context_lens)), int(np.argmin(wl.context_lens))})
+    return [(b, h) for b in seqs for h in range(wl.spec.n_heads)]
+
+
+def test_pools_beyond_4gib():
+    """The small GQA workload moved to the top of a 4.6 GB pool: every block offset exceeds
+    2^32 bytes; append and decode must match the oracle on the original placement."""
+    wl = wlm.make_workload(3, small=True)
+    nb, bs, Hkv, d = wl.k_pool.shape
+    block_bytes = bs * Hkv * d * 2
+    big = (1 << 32) // block_bytes + nb + 8           # highest block ends past 4 GiB + nb blocks
+    base = big - nb
+    _log(f"pools of {big} blocks ({2 * big * block_bytes / 1e9:.1f} GB)")
+    t = wlm.to_torch(wl, DEV)
+    kbig = torch.empty((big, bs, Hkv, d), dtype=torch.bfloat16, device=DEV)
+    vbig = torch.empty_like(kbig)
+    kbig[base:] = t["k_pool"]
+    vbig[base:] = t["v_pool"]
+    tables = t["block_tables"].clone()
+    used = tables >= 0
+    tables[used] += base
+    pkv.pkv_kv_append(kbig, vbig, t["k_new"], t["v_new"], tables, t["positions"])
+    out = torch.empty_like(t["q"])
+    pkv.pkv_paged_decode_attention(out, t["q"], kbig, vbig, tables, t["context_lens"],
+                                   wl.max_context_len, wl.scale)
+    torch.cuda.synchronize()
+    kp, vp = orc.kv_append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.block_tables,
+                           wl.positions, 16)
+    assert np.array_equal(wlm.from_torch(kbig[base:], "bf16"), kp)
+    assert np.array_equal(wlm.from_torch(vbig[base:], "bf16"), vp)
+    ref = orc.paged_decode_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                     wl.scale, "bf16")
+    assert_close(out.double().cpu().numpy(), ref, "bf16", "pool beyond 4 GiB")
+
+
+def test_more_sequences_than_the_split_mode_holds():
+    """4100 sequences (> 4096): the library falls back to fixed 512-token partitions; a few
+    long sequences span several of them."""
+    lengths = [int(x) for x in np.random.default_rng(41).integers(1, 300, size=4100)]
+    lengths[5], lengths[3000], lengths[4099] = 5000, 1030, 513
+    spec = wlm.Spec("many-seqs-bf16", "bf16", 4100, 16, 8, 64, "gqa", lengths=tuple(lengths))
+    wl = wlm.make_workload(spec, seed=41)
+    assert pkv.pkv_decode_workspace_bytes(4100, 16, 8, 64, wl.max_context_len, 0) == \
+        pkv.pkv_decode_workspace_bytes(4100, 16, 8, 64, wl.max_context_len, 512)
+    t = wlm.to_torch(wl, DEV)
+    pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                      t["positions"])
+    got = _decode(t, wl)
+    pairs = _sampled(wl, 40, 41) + [(b, h) for b in (5, 3000, 4099) for h in range(16)]
+    ref = _oracle(wl, pairs)
+    b = np.array([p[0] for p in pairs])
+    h = np.array([p[1] for p in pairs])
+    assert_close(got[b, h], ref[b, h], "bf16", "4100 sequences")
+    assert np.isfinite(got).all()
+
+
+def test_batch_at_the_split_mode_limit():
+    """4096 sequences, a few of them long: the balanced split at its largest batch."""
+    lengths = [int(x) for x in np.random.default_rng(42).integers(1, 300, size=4096)]
+    lengths[7], lengths[2000], lengths[4095] = 6000, 9000, 2500
+    spec = wlm.Spec("split-limit-bf16", "bf16", 4096, 16, 8, 64, "gqa", lengths=tuple(lengths))
+    wl = wlm.make_workload(spec, seed=42)
+    t = wlm.to_torch(wl, DEV)
+    pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                      t["positions"])
+    got = _decode(t, wl)
+    pairs = _sampled(wl, 30, 42) + [(b, h) for b in (7, 2000, 4095) for h in range(16)]
+    ref = _oracle(wl, pairs)
+    b = np.array([p[0] for p in pairs])
+    h = np.array([p[1] for p in pairs])
+    assert_close(got[b, h], ref[b, h], "bf16", "4096 sequences")
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("ptok", [0, 256])
+def test_sequence_filling_its_whole_table(ptok):
+    """max_context_len = max_blocks_per_seq * 16: the last token is the last slot of the
+    last table entry."""
+    spec = wlm.Spec("full-table-f16", "f16", 3, 32, 8, 128, "gqa", lengths=(1599, 700, 31))
+    wl = wlm.make_workload(spec, seed=43)
+    assert wl.max_context_len == wl.block_tables.shape[1] * 16
+    t = wlm.to_torch(wl, DEV)
+    pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                      t["positions"])
+    assert_close(_decode(t, wl, ptok), _oracle(wl), "f16", "full table")
+
+
+@pytest.mark.parametrize("dtype,H,Hkv", [("bf16", 48, 12), ("f16", 12, 12), ("bf16", 40, 5)])
+def test_kv_heads_not_a_multiple_of_8(dtype, H, Hkv):
+    """Four-wave workgroups; the last one holds fewer heads than waves."""
+    spec = wlm.Spec(f"hkv{Hkv}-{dtype}", dtype, 5, H, Hkv, 128, "gqa", len_range=(1, 1500))
+    wl = wlm.make_workload(spec, seed=H + Hkv)
+    t = wlm.to_torch(wl, DEV)
+    pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                      t["positions"])
+    for ptok in (0, 128):
+        assert_close(_decode(t, wl, ptok), _oracle(wl), dtype, f"Hkv {Hkv} P {ptok}")

@@ -153,7 +153,7 @@ def test_partition_size_invariance_fp32():
 
 
 # ---------------------------------------------------------------------------------------
-# Full-size workloads, the launch configuration the benchmark times (512-token partitions),
+# Full-size workloads in the launch configuration the benchmark times (balanced split),
 # sampled outputs computed one by one by the oracle
 # ---------------------------------------------------------------------------------------
 
