@@ -1,10 +1,13 @@
 """Benchmark of one paged decode step (append + attention) on one MI355X.
 
-A step is one pass of the whole path over one batch: pkv_kv_append writes every
-sequence's new token into its slot, then pkv_paged_decode_attention (the split-KV decode
-kernel, plus the merge kernel when a sequence spans several partitions) attends over the
-paged context. Inputs are seeded synthetic workloads resident in HBM before timing; the
-same step is repeated (the new token is rewritten into the same slot, so every step does
+A step is one pass of the whole path over one batch: every sequence's new token is
+written into its slot and attention runs over the paged context. By default the step is one
+pkv_paged_decode_step launch (the split-KV decode kernel takes the new token's K/V straight
+from the input rows and stores them into the pool, plus the merge kernel when a sequence
+spans several partitions); --separate-append times pkv_kv_append followed by
+pkv_paged_decode_attention instead, and the default line also reports that two-launch
+step's time. Inputs are seeded synthetic workloads resident in HBM before timing; the same
+step is repeated (the new token is rewritten into the same slot, so every step does
 identical work).
 
 Prints ONE JSON line: the metric is KV GB/s read (whole step), with the decode launch's
@@ -12,6 +15,7 @@ achieved bandwidth against the 8 TB/s HBM peak in "roofline", and the fp64 CPU o
 on a bounded sample of the same workload in "cpu_baseline".
 
     python bench.py [--steps K] [--warmup W] [--config 2] [--partition 0] [--all]
+                    [--separate-append]
 """
 
 from __future__ import annotations
@@ -34,17 +38,18 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 
 # HBM bytes per decode launch (decode + merge kernels) from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE runs, each scaled by what the counter reads for a 1 GiB device copy, keyed by
-# (workload id, partition_tokens). Each entry records the sha256 prefix of the decode kernel
-# source it was measured on; it is reported only while that source is unchanged.
+# (workload id, partition_tokens, fused step). Each entry records the sha256 prefix of the
+# decode kernel source it was measured on; it is reported only while that source is
+# unchanged.
 MEASURED_TRAFFIC = {
-    (2, 0): {"bytes": 1193268269, "decode_source_sha256": "0a62aded8d9a1841"},
+    (2, 0, False): {"bytes": 1193268269, "decode_source_sha256": "0a62aded8d9a1841"},
 }
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", "pkv_decode.hip")
 
 
-def measured_traffic(cfg: int, partition: int):
+def measured_traffic(cfg: int, partition: int, fused: bool):
     import hashlib
-    entry = MEASURED_TRAFFIC.get((cfg, partition))
+    entry = MEASURED_TRAFFIC.get((cfg, partition, fused))
     if entry is None:
         return None
     with open(DECODE_SOURCE, "rb") as f:
@@ -61,6 +66,9 @@ def parse():
     ap.add_argument("--partition", type=int, default=0,
                     help="tokens per KV partition; 0 = the library's balanced split")
     ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="time pkv_kv_append + pkv_paged_decode_attention (two launches) "
+                         "instead of the fused pkv_paged_decode_step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after timing, copy a buffer of this many MiB 3 times (a dispatch of "
@@ -112,40 +120,73 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(mid_event):
+    def separate_step(mid_event=None):
         pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"],
                           t["block_tables"], t["positions"], stream=stream)
-        mid_event.record(stream)
+        if mid_event is not None:
+            mid_event.record(stream)
         pkv.pkv_paged_decode_attention(out, t["q"], t["k_pool"], t["v_pool"],
                                        t["block_tables"], t["context_lens"],
                                        wl.max_context_len, wl.scale, args.partition, ws, stream)
 
-    scratch_event = torch.cuda.Event(enable_timing=True)
-    for _ in range(args.warmup):
-        step(scratch_event)
-    torch.cuda.synchronize()
+    def fused_step(mid_event=None):
+        if mid_event is not None:
+            mid_event.record(stream)
+        pkv.pkv_paged_decode_step(out, t["q"], t["k_pool"], t["v_pool"], t["k_new"],
+                                  t["v_new"], t["block_tables"], t["context_lens"],
+                                  wl.max_context_len, wl.scale, args.partition, ws, stream)
 
+    fused = not args.separate_append
+    step = fused_step if fused else separate_step
     K = args.steps
-    ev_start = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_mid = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(K):
-        ev_start[i].record(stream)
-        step(ev_mid[i])
-        ev_end[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
 
-    step_ms = np.array([ev_start[i].elapsed_time(ev_end[i]) for i in range(K)])
-    dec_ms = np.array([ev_mid[i].elapsed_time(ev_end[i]) for i in range(K)])
-    total_ms = ev_start[0].elapsed_time(ev_end[K - 1])
+    def run(fn, per_step):
+        """K steps after W warm-up ones; per_step brackets each step (and, for the
+        two-launch step, its decode launch) with events, otherwise only the K-step
+        region is bracketed."""
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            if per_step:
+                ev[i][0].record(stream)
+                fn(ev[i][1] if fn is separate_step else None)
+                ev[i][2].record(stream)
+            else:
+                fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - w0
+        total = e0.elapsed_time(e1)
+        if not per_step:
+            return total, wall_s, None, None
+        st = np.array([e[0].elapsed_time(e[2]) for e in ev])
+        la = (np.array([e[1].elapsed_time(e[2]) for e in ev]) if fn is separate_step else st)
+        return total, wall_s, st, la
+
+    # The timed region. The fused step is one launch, so the region's time per step is
+    # that launch's duration (inter-launch gaps included) and no per-step events (each
+    # costs a few microseconds of GPU time) are recorded in it; the two-launch step
+    # brackets its decode launch with events to time it apart from the append.
+    total_ms, wall, step_ms, dec_ms = run(step, per_step=not fused)
     ms_per_step = total_ms / K
     by = algorithmic_bytes(wl)
     value = by["kv"] / (ms_per_step * 1e-3) / 1e9
-    dec_avg_s = float(dec_ms.mean()) * 1e-3
-    achieved = by["decode"] / dec_avg_s / 1e9
+    dec_avg_s = ms_per_step * 1e-3 if fused else float(dec_ms.mean()) * 1e-3
+    launch_bytes = by["decode"] + (by["append"] if fused else 0)
+    achieved = launch_bytes / dec_avg_s / 1e9
+    # After the timed region: per-step event spread of the fused step, and the other
+    # form of the step timed like the timed region.
+    if fused:
+        _, _, step_ms, _ = run(step, per_step=True)
+        dec_ms = step_ms
+    other = separate_step if fused else fused_step
+    other_us = run(other, per_step=False)[0] / K * 1e3
 
     spec = wl.spec
     res = {
@@ -171,6 +212,8 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
             "max_context_len": wl.max_context_len,
             "kv_split": ("balanced split over the GPU" if args.partition == 0
                          else f"fixed {args.partition}-token partitions"),
+            "step": ("one launch: append fused into the decode kernel (pkv_paged_decode_step)"
+                     if fused else "two launches: pkv_kv_append + pkv_paged_decode_attention"),
             "kv_bytes_per_step": by["kv"], "kv_unique_bytes_per_step": by["kv_unique"],
             "parallelism": "single GPU",
         },
@@ -178,21 +221,26 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
             "step_us_median": round(float(np.median(step_ms)) * 1e3, 2),
             "step_us_p10": round(float(np.percentile(step_ms, 10)) * 1e3, 2),
             "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+            "step_spread_from": ("a second run of K steps with per-step events" if fused
+                                 else "per-step events in the timed region"),
             "decode_us_mean": round(dec_avg_s * 1e6, 2),
             "decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
             "decode_kv_gbps": round(by["kv"] / dec_avg_s / 1e9, 2),
+            ("separate_step_us" if fused else "fused_step_us"): round(other_us, 2),
             "host_wall_us_per_step": round(wall / K * 1e6, 2),
             "workload_gen_s": round(gen_s, 1),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged decode launch (decode kernel + partition merge)",
+            "kernel": ("paged decode step launch (decode kernel with the fused append + "
+                       "partition merge)" if fused else
+                       "paged decode launch (decode kernel + partition merge)"),
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": measured_traffic(cfg, args.partition),
-            "algorithmic_bytes_per_launch": by["decode"],
+            "traffic": measured_traffic(cfg, args.partition, fused),
+            "algorithmic_bytes_per_launch": launch_bytes,
         },
     }
     res["ceiling"] = stream_ceiling(by["kv"], dev)

@@ -160,6 +160,28 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
                                    hipStream_t stream);
 
 /*
+ * pkv_paged_decode_step - pkv_kv_append followed by pkv_paged_decode_attention, in one
+ * launch. Source: the new token's K/V enter the cache before attention
+ * ("09-inference-optimization", KV Cache; "LLM 推理优化全景实战" §2.3 write_kv).
+ * The appended token of sequence b is token context_lens[b] - 1 (positions are implied);
+ * k_new, v_new [num_seqs, n_kv_heads, d_head] in dtype. The wave that attends over the
+ * block holding that token takes the token's K/V straight from k_new / v_new and writes
+ * them into the pool slot, so the pools afterwards equal those of the two separate calls
+ * and `out` equals their result (same arithmetic). Sequences whose length is invalid get
+ * NaN outputs and no append; a table entry outside the pool skips the write (NaN output).
+ * k_pool, v_pool are written; the other arguments are those of pkv_paged_decode_attention
+ * (workspace size from pkv_decode_workspace_bytes).
+ */
+int32_t pkv_paged_decode_step(void* out, const void* q, void* k_pool, void* v_pool,
+                              const void* k_new, const void* v_new, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, int32_t num_blocks,
+                              int32_t max_context_len, int32_t block_size, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t d_head, float scale,
+                              int32_t partition_tokens, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * pkv_decode_workspace_bytes - scratch bytes pkv_paged_decode_attention needs for these
  * sizes (host only, no device call). 0 when no partial results are needed (fixed
  * partitions with every sequence in one partition). Returns 0 for invalid sizes as well;

@@ -123,8 +123,10 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
                     int32_t n_kv_heads, int32_t d_head, float scale, int32_t partition_tokens,
                     int32_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
                     int32_t kv_format = 0, const float* k_scales = nullptr,
-                    const float* v_scales = nullptr) {
+                    const float* v_scales = nullptr, const void* k_new = nullptr,
+                    const void* v_new = nullptr, bool fused_append = false) {
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
+  if (fused_append && (!k_new || !v_new)) return PKV_ERR_NULL;
   if (kv_format != 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
   int32_t st = check_pool_args(num_seqs, max_blocks_per_seq, num_blocks, max_context_len,
                                block_size, n_kv_heads, d_head, dtype);
@@ -140,6 +142,7 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   if (partition_tokens < 0 || partition_tokens % pkv::kBlockTokens) return PKV_ERR_PARTITION;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKV_ERR_ALIGN;
+  if (fused_append && (!aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_ALIGN;
   const size_t eb = (size_t)elem_bytes(dtype);
   const size_t out_bytes = (size_t)num_seqs * q_len * n_heads * d_head * eb;
   const size_t pool_bytes =
@@ -151,6 +154,14 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   if (kv_format != 0 && (overlaps(out, out_bytes, k_scales, scale_bytes) ||
                          overlaps(out, out_bytes, v_scales, scale_bytes)))
     return PKV_ERR_ALIAS;
+  if (fused_append) {
+    const size_t new_bytes = (size_t)num_seqs * n_kv_heads * d_head * eb;
+    if (overlaps(out, out_bytes, k_new, new_bytes) || overlaps(out, out_bytes, v_new, new_bytes) ||
+        overlaps(k_new, new_bytes, k_pool, pool_bytes) || overlaps(k_new, new_bytes, v_pool, pool_bytes) ||
+        overlaps(v_new, new_bytes, k_pool, pool_bytes) || overlaps(v_new, new_bytes, v_pool, pool_bytes) ||
+        overlaps(k_pool, pool_bytes, v_pool, pool_bytes))
+      return PKV_ERR_ALIAS;
+  }
 
   const Plan plan = make_plan(num_seqs, q_len, n_heads, n_kv_heads, d_head, max_context_len,
                               partition_tokens);
@@ -187,6 +198,8 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   }
   a.k_scales = k_scales;
   a.v_scales = v_scales;
+  a.k_new = fused_append ? static_cast<const char*>(k_new) : nullptr;
+  a.v_new = fused_append ? static_cast<const char*>(v_new) : nullptr;
   const hipError_t e =
       kv_format ? pkv::launch_decode_quantized(a, dtype, kv_format, d_head, n_heads / n_kv_heads,
                                                stream)
@@ -314,6 +327,20 @@ int32_t pkv_kv_append_quantized(void* k_codes, void* v_codes, float* k_scales, f
   a.dtype = dtype;
   a.kv_format = kv_format;
   return pkv::launch_append_quantized(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int32_t pkv_paged_decode_step(void* out, const void* q, void* k_pool, void* v_pool,
+                              const void* k_new, const void* v_new, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t max_blocks_per_seq, int32_t num_blocks,
+                              int32_t max_context_len, int32_t block_size, int32_t n_heads,
+                              int32_t n_kv_heads, int32_t d_head, float scale,
+                              int32_t partition_tokens, int32_t dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, 1,
+                     max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
+                     n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
+                     workspace_bytes, stream, 0, nullptr, nullptr, k_new, v_new, true);
 }
 
 int32_t pkv_paged_decode_attention_quantized(

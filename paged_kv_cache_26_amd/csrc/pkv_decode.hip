@@ -163,6 +163,48 @@ __device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kblk, cons
   }
 }
 
+// Token 4r + JJ's V chunk of this lane into t.v[JJ] (kVW 32-bit words from src).
+template <int DT, int D, bool NT_V, int JJ>
+__device__ __forceinline__ void load_v_chunk(Tile<DT, D>& t, const char* src) {
+  using G_ = Geo<DT, D>;
+  if constexpr (G_::kVW == 8) {
+    const u32x4 a0 = load_v<u32x4, NT_V>(src);
+    const u32x4 a1 = load_v<u32x4, NT_V>(src + 16);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) { t.v[JJ][x] = a0[x]; t.v[JJ][4 + x] = a1[x]; }
+  } else if constexpr (G_::kVW == 4) {
+    const u32x4 a0 = load_v<u32x4, NT_V>(src);
+#pragma unroll
+    for (int x = 0; x < 4; ++x) t.v[JJ][x] = a0[x];
+  } else {
+    const u32x2 a0 = load_v<u32x2, NT_V>(src);
+    t.v[JJ][0] = a0[0];
+    t.v[JJ][1] = a0[1];
+  }
+}
+
+// load_tile for the block that receives the appended token (fused append): the lanes
+// that hold slot `off` read its K and V from the token's new rows (k_row / v_row: its K/V
+// row for this KV head in k_new / v_new) instead of from the pool. Issued with the other
+// prefetches, so the new rows add no wait of their own.
+template <int DT, int D, bool NT_V>
+__device__ __forceinline__ void load_tile_new(Tile<DT, D>& t, const char* kblk, const char* vblk,
+                                              uint32_t k_lane, uint32_t v_lane,
+                                              uint32_t tok_stride, const char* k_row,
+                                              const char* v_row, int off, int lane) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  const char* kp = c == off ? k_row + 16 * r : kblk + k_lane;
+#pragma unroll
+  for (int kk = 0; kk < G_::kNK; ++kk) t.k[kk] = *reinterpret_cast<const u32x4*>(kp + 64 * kk);
+  static_for<4>([&](auto jc) {
+    constexpr int jj = decltype(jc)::value;
+    const bool mine = jj == (off & 3) && r == (off >> 2);
+    load_v_chunk<DT, D, NT_V, jj>(t, mine ? v_row + c * (G_::kEPL * G_::kE)
+                                          : vblk + (v_lane + jj * tok_stride));
+  });
+}
+
 template <int DT, int D, int G>
 struct WaveState {
   float m = -INFINITY;                 // running max (base 2) of head c
@@ -278,7 +320,7 @@ __device__ __forceinline__ void store_row_chunk(void* base, size_t idx, const fl
 
 // Stream blocks [blk_begin, blk_begin + n_my) of sequence b through one wave: table
 // entries are preloaded 64 at a time into a VGPR, the tiles of the next kDepth blocks are in
-// flight (`load(tile, physical_block)`) while `process(tile, first_token_of_block)` runs on
+// flight (`load(tile, physical_block, logical_block)`) while `process(tile, first_token_of_block)` runs on
 // the current one. bad is set if a table entry is outside the pool (that block's data is
 // then not read).
 template <typename TileT, int kDepth, typename L, typename F>
@@ -294,7 +336,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
     int pb = __builtin_amdgcn_readlane(tbl, i & 63);
     const bool ok = (unsigned)pb < (unsigned)a.num_blocks;
     bad |= !ok;
-    load(t, ok ? pb : 0);
+    load(t, ok ? pb : 0, blk_begin + i);
   };
 
   constexpr int NB = kDepth + 1;
@@ -317,10 +359,13 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
   }
 }
 
-// stream_tiles over the K/V pools of KV head j in the storage dtype.
-template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true, typename F>
+// stream_tiles over the K/V pools of KV head j in the storage dtype. kNew (fused append):
+// the slot of token new_tok is read from the new K/V rows of (b, j) (load_tile_new).
+template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true, bool kNew = false,
+          typename F>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
-                                              int n_my, int lane, int& bad, F&& process) {
+                                              int n_my, int lane, int& bad, F&& process,
+                                              int new_tok = -1) {
   using G_ = Geo<DT, D>;
   const int r = lane >> 4, c = lane & 15;
   const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;    // bytes between tokens
@@ -330,9 +375,18 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
   const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
   stream_tiles<Tile<DT, D>, kDepth>(
       a, b, blk_begin, n_my, lane, bad,
-      [&](Tile<DT, D>& t, int pb) {
-        load_tile<DT, D, NT_V>(t, a.k_pool + (size_t)pb * blk_stride,
-                               a.v_pool + (size_t)pb * blk_stride, k_lane, v_lane, tok_stride);
+      [&](Tile<DT, D>& t, int pb, int blk) {
+        const char* kb = a.k_pool + (size_t)pb * blk_stride;
+        const char* vb = a.v_pool + (size_t)pb * blk_stride;
+        if constexpr (kNew) {
+          if (blk == (new_tok >> 4)) {
+            const size_t row = ((size_t)b * a.n_kv_heads + j) * G_::kRow;
+            load_tile_new<DT, D, NT_V>(t, kb, vb, k_lane, v_lane, tok_stride, a.k_new + row,
+                                       a.v_new + row, new_tok & (kBlockTokens - 1), lane);
+            return;
+          }
+        }
+        load_tile<DT, D, NT_V>(t, kb, vb, k_lane, v_lane, tok_stride);
       },
       process);
 }
@@ -353,20 +407,60 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, bool used, size_
 
 // One wave: blocks [blk_begin, blk_begin + n_my) of sequence b, KV head j, into st
 // (lane-partial; finish_rows completes it). Tokens >= tok_end are masked.
-template <int DT, int D, int G>
+// Fused append (kAppend): the tile of the block holding token t_new = N_b - 1 (the one
+// appended by this launch) was loaded with that token's K/V from k_new / v_new; this
+// stores them from the tile into the token's pool slot (table[b][t_new / 16], t_new % 16).
+// Exactly one wave per (b, j) processes that block and no other wave of the launch reads
+// the slot, so the store needs no ordering within the launch. An out-of-range table entry
+// skips the store (the sequence's output is NaN anyway).
+template <int DT, int D>
+__device__ __forceinline__ void store_new_slot(const DecodeArgs& a, const Tile<DT, D>& t, int b,
+                                               int j, int t_new, int lane) {
+  using G_ = Geo<DT, D>;
+  const int r = lane >> 4, c = lane & 15;
+  const int off = t_new & (kBlockTokens - 1);
+  const int pb = a.block_tables[(size_t)b * a.max_blocks_per_seq + (t_new >> 4)];
+  if ((unsigned)pb >= (unsigned)a.num_blocks) return;
+  const size_t dst = (((size_t)pb * kBlockTokens + off) * a.n_kv_heads + j) * G_::kRow;
+  if (c == off) {                 // K row: this lane's 16-byte pieces at 64 kk + 16 r
+    char* kd = const_cast<char*>(a.k_pool) + dst + 16 * r;
+#pragma unroll
+    for (int kk = 0; kk < G_::kNK; ++kk) *reinterpret_cast<u32x4*>(kd + 64 * kk) = t.k[kk];
+  }
+  if (r == (off >> 2)) {          // V row: this lane's chunk c of token 4r + (off & 3)
+    unsigned* vd = reinterpret_cast<unsigned*>(const_cast<char*>(a.v_pool) + dst +
+                                               (size_t)c * (G_::kEPL * G_::kE));
+    // select token (off & 3) of the lane's four with masks: a branch per token lets the
+    // compiler index the tile with a run-time value, which moves the tiles to scratch
+    const int sj = off & 3;
+#pragma unroll
+    for (int x = 0; x < G_::kVW; ++x) {
+      unsigned w = 0;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) w |= t.v[jj][x] & (jj == sj ? ~0u : 0u);
+      vd[x] = w;
+    }
+  }
+}
+
+template <int DT, int D, int G, bool kAppend>
 __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const DecodeArgs& a,
                                        int b, int j, int blk_begin, int n_my, int tok_end,
-                                       int lane) {
+                                       int n_ctx, int lane) {
   const int r = lane >> 4, c = lane & 15;
   u32x4 qf[Geo<DT, D>::kNK];
   load_query<DT, D>(a, c < G, (size_t)b * a.n_heads + (size_t)j * G + c, r, qf);
-  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
+  const int t_new = n_ctx - 1;                    // the appended token (kAppend)
+  stream_blocks<DT, D, Geo<DT, D>::kDepth, true, kAppend>(
+      a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
+    if constexpr (kAppend)
+      if (tok0 == (t_new & ~(kBlockTokens - 1))) store_new_slot<DT, D>(a, t, b, j, t_new, lane);
     // only the last block of a sequence can be partial (partitions are block aligned)
     if (tok0 + kBlockTokens > tok_end)
       process_block<DT, D, G, true>(st, t, qf, tok0, tok_end, a.scale_log2, r);
     else
       process_block<DT, D, G, false>(st, t, qf, tok0, tok_end, a.scale_log2, r);
-  });
+  }, t_new);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -823,7 +917,7 @@ __device__ __forceinline__ void attend_q(QState<DT, D>& st, int& bad, const Deco
   const char* vc = static_cast<const char*>(a.v_pool);
   stream_tiles<QTile<D>, 2>(
       a, b, blk_begin, n_my, lane, bad,
-      [&](QTile<D>& t, int pb) {
+      [&](QTile<D>& t, int pb, int) {
         const char* kb = kc + (size_t)pb * blk_stride;
         const char* vb = vc + (size_t)pb * blk_stride;
 #pragma unroll
@@ -943,9 +1037,10 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, i
       write_final_mq<DT, D, G>(a, st, bad, b, j, lane);
     else
       write_record_mq<DT, D, G>(a, st, bad, lane, rec);
-  } else if constexpr (MODE == kModeSingle) {
+  } else if constexpr (MODE == kModeSingle || MODE == kModeSingleAppend) {
     WaveState<DT, D, G> st;
-    attend<DT, D, G>(st, bad, a, b, j, blk_begin, n_my, tok_end, lane);
+    attend<DT, D, G, MODE == kModeSingleAppend>(st, bad, a, b, j, blk_begin, n_my, tok_end,
+                                                n_ctx, lane);
     finish_rows<DT, D, G>(st);
     if (whole)
       write_final<DT, D, G>(a, st, bad, (size_t)b * a.n_heads + (size_t)j * G, lane);
@@ -1359,7 +1454,9 @@ hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
 
 template <int DT, int D, int G, int NW>
 hipError_t launch_mq(const DecodeArgs& a, hipStream_t stream) {
-  if (a.q_len == 1) return launch_typed<DT, D, G, NW, kModeSingle>(a, stream);
+  if (a.q_len == 1)
+    return a.k_new ? launch_typed<DT, D, G, NW, kModeSingleAppend>(a, stream)
+                   : launch_typed<DT, D, G, NW, kModeSingle>(a, stream);
   return launch_typed<DT, D, G, NW, kModeMulti>(a, stream);
 }
 

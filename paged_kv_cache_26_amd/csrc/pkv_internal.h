@@ -24,6 +24,7 @@ constexpr int kModeSingle = 0;      // one query per sequence, P.V on the vector
 constexpr int kModeMulti = 1;       // q_len queries per sequence, P.V on the matrix cores
 constexpr int kModeQuantInt8 = 2;   // one query, INT8 codes + (s, z) per token and KV head
 constexpr int kModeQuantFp8 = 3;    // one query, E4M3 codes + (s, 0) per token and KV head
+constexpr int kModeSingleAppend = 4; // kModeSingle that also appends the new token (k_new)
 
 // Waves per decode workgroup (one KV head each) used with this many KV heads. The
 // launcher may use fewer (4) for kernels that do not fit 256 registers per lane; this is
@@ -90,6 +91,10 @@ struct DecodeArgs {
   // [num_blocks][n_kv_heads][16][2] fp32.
   const float* k_scales;
   const float* v_scales;
+  // Fused append (single query, dtype pools): the new token's K / V rows,
+  // [num_seqs][n_kv_heads][d_head]; the token is context_lens[b] - 1. nullptr: no append.
+  const char* k_new;
+  const char* v_new;
 };
 
 // Quantizing append: one token per sequence, K and V rows of every KV head quantized to

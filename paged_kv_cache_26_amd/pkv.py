@@ -72,6 +72,9 @@ _SIGNATURES = {
     "pkv_paged_decode_attention_quantized": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 8 +
                                              [ctypes.c_float, _c_i32, _c_i32, _c_i32, _c_ptr,
                                               _c_size, _c_ptr]),
+    "pkv_paged_decode_step": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 8 + [ctypes.c_float, _c_i32,
+                                                                     _c_i32, _c_ptr, _c_size,
+                                                                     _c_ptr]),
     "pkv_stream_read": (_c_i32, [_c_ptr, _c_size, _c_ptr, _c_size, _c_i32, _c_ptr]),
     "pkv_find_shared_prefixes": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr,
                                           _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
@@ -193,6 +196,35 @@ def pkv_paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_len
         _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_paged_decode_attention")
+    return out
+
+
+def pkv_paged_decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                          max_context_len: int, scale: float | None = None,
+                          partition_tokens: int = 0, workspace=None, stream=None):
+    """pkv_kv_append (token context_lens[b] - 1) and pkv_paged_decode_attention in one
+    launch. Returns out."""
+    lib = load_library()
+    _check_device(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens)
+    _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype ==
+             k_new.dtype == v_new.dtype, "q, out, pools and new rows must share a dtype")
+    _require(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, H, d]")
+    _require(k_new.shape == v_new.shape and k_new.shape == (q.shape[0], k_pool.shape[2], q.shape[2]),
+             "k_new/v_new must be [B, H_kv, d]")
+    B, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = pkv_decode_workspace_bytes(B, H, k_pool.shape[2], d, max_context_len, partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pkv_paged_decode_step(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+        _ptr(block_tables), _ptr(context_lens), B, block_tables.shape[1], k_pool.shape[0],
+        int(max_context_len), k_pool.shape[1], H, k_pool.shape[2], d, float(scale),
+        int(partition_tokens), _DTYPE_CODE[q.dtype], _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_paged_decode_step")
     return out
 
 

@@ -203,3 +203,15 @@ def test_stream_read_rejects_bad_arguments_on_host(lib):
     assert f(0x1000, 1000, 0x2000, 1 << 20, 4, None) == -2      # not a multiple of 16
     assert f(0x1008, 1024, 0x2000, 1 << 20, 4, None) == -11
     assert f(0x1000, 1024, 0x2000, 1023, 4, None) == -9         # sink shorter than 4 * 256
+
+
+def test_fused_step_rejects_bad_arguments_on_host(lib):
+    f = lib.pkv_paged_decode_step
+    good = [0x1000000, 0x2000000, 0x10000000, 0x20000000, 0x3000000, 0x4000000, 0x30000,
+            0x40000, 4, 64, 64, 700, 16, 32, 8, 128, 0.1, 0, 2, 0, 0, None]
+    for idx, val, code in [(4, 0, -1), (5, 0, -1), (4, 0x3000008, -11), (4, 0x1000000, -12),
+                           (5, 0x10000000, -12), (18, 3, -3)]:
+        args = list(good)
+        args[idx] = val
+        assert f(*args) == code, (idx, val)
+    assert f(*good) == -9                     # the balanced split needs its workspace

@@ -1,0 +1,36 @@
+"""The benchmark's command line on the CPU: one GPU only, and the algorithmic byte counts
+it reports."""
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+from paged_kv_cache_26_amd import workload as wlm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
+
+
+def test_algorithmic_bytes_of_the_tiny_step():
+    wl = wlm.make_workload(1)                 # 4 sequences, 4 heads, d 64, fp32
+    by = bench.algorithmic_bytes(wl)
+    n = wl.context_lens.astype(int)
+    assert by["kv"] == int(n.sum()) * 2 * 4 * 64 * 4           # K and V rows read
+    assert by["decode"] == by["kv"] + 2 * 4 * 4 * 64 * 4 + \
+        int(sum(-(-x // 16) for x in n)) * 4 + 4 * 4           # q + out, tables, lengths
+    assert by["append"] == 2 * 2 * 4 * 4 * 64 * 4 + 4 * 4 * 2   # rows read + written
+
+
+def test_measured_traffic_is_dropped_when_the_kernel_source_changes(monkeypatch):
+    monkeypatch.setitem(bench.MEASURED_TRAFFIC, (9, 0, True),
+                        {"bytes": 123, "decode_source_sha256": "0" * 16})
+    assert bench.measured_traffic(9, 0, True) is None
+    assert bench.measured_traffic(9, 64, True) is None
