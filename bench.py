@@ -42,7 +42,8 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 # decode kernel source it was measured on; it is reported only while that source is
 # unchanged.
 MEASURED_TRAFFIC = {
-    (2, 0, False): {"bytes": 1193268269, "decode_source_sha256": "0a62aded8d9a1841"},
+    (2, 0, True): {"bytes": 1194385617, "decode_source_sha256": "09a4609d52223e72"},
+    (2, 0, False): {"bytes": 1193299792, "decode_source_sha256": "09a4609d52223e72"},
 }
 DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", "pkv_decode.hip")
 
@@ -60,8 +61,12 @@ def measured_traffic(cfg: int, partition: int, fused: bool):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 200 for the decode step, 50 otherwise)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 1000 for the decode step, about 0.2 s: "
+                         "the GPU's clocks settle over the first tens of milliseconds of load; "
+                         "10 otherwise)")
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--partition", type=int, default=0,
                     help="tokens per KV partition; 0 = the library's balanced split")
@@ -87,7 +92,13 @@ def parse():
     ap.add_argument("--q-len", type=int, default=4, help="new tokens per sequence (multi-query)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
-    return ap.parse_args()
+    args = ap.parse_args()
+    decode = args.component == "decode"
+    if args.steps is None:
+        args.steps = 200 if decode else 50
+    if args.warmup is None:
+        args.warmup = 1000 if decode else 10
+    return args
 
 
 def algorithmic_bytes(wl) -> dict:

@@ -163,48 +163,6 @@ __device__ __forceinline__ void load_tile(Tile<DT, D>& t, const char* kblk, cons
   }
 }
 
-// Token 4r + JJ's V chunk of this lane into t.v[JJ] (kVW 32-bit words from src).
-template <int DT, int D, bool NT_V, int JJ>
-__device__ __forceinline__ void load_v_chunk(Tile<DT, D>& t, const char* src) {
-  using G_ = Geo<DT, D>;
-  if constexpr (G_::kVW == 8) {
-    const u32x4 a0 = load_v<u32x4, NT_V>(src);
-    const u32x4 a1 = load_v<u32x4, NT_V>(src + 16);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) { t.v[JJ][x] = a0[x]; t.v[JJ][4 + x] = a1[x]; }
-  } else if constexpr (G_::kVW == 4) {
-    const u32x4 a0 = load_v<u32x4, NT_V>(src);
-#pragma unroll
-    for (int x = 0; x < 4; ++x) t.v[JJ][x] = a0[x];
-  } else {
-    const u32x2 a0 = load_v<u32x2, NT_V>(src);
-    t.v[JJ][0] = a0[0];
-    t.v[JJ][1] = a0[1];
-  }
-}
-
-// load_tile for the block that receives the appended token (fused append): the lanes
-// that hold slot `off` read its K and V from the token's new rows (k_row / v_row: its K/V
-// row for this KV head in k_new / v_new) instead of from the pool. Issued with the other
-// prefetches, so the new rows add no wait of their own.
-template <int DT, int D, bool NT_V>
-__device__ __forceinline__ void load_tile_new(Tile<DT, D>& t, const char* kblk, const char* vblk,
-                                              uint32_t k_lane, uint32_t v_lane,
-                                              uint32_t tok_stride, const char* k_row,
-                                              const char* v_row, int off, int lane) {
-  using G_ = Geo<DT, D>;
-  const int r = lane >> 4, c = lane & 15;
-  const char* kp = c == off ? k_row + 16 * r : kblk + k_lane;
-#pragma unroll
-  for (int kk = 0; kk < G_::kNK; ++kk) t.k[kk] = *reinterpret_cast<const u32x4*>(kp + 64 * kk);
-  static_for<4>([&](auto jc) {
-    constexpr int jj = decltype(jc)::value;
-    const bool mine = jj == (off & 3) && r == (off >> 2);
-    load_v_chunk<DT, D, NT_V, jj>(t, mine ? v_row + c * (G_::kEPL * G_::kE)
-                                          : vblk + (v_lane + jj * tok_stride));
-  });
-}
-
 template <int DT, int D, int G>
 struct WaveState {
   float m = -INFINITY;                 // running max (base 2) of head c
@@ -320,7 +278,7 @@ __device__ __forceinline__ void store_row_chunk(void* base, size_t idx, const fl
 
 // Stream blocks [blk_begin, blk_begin + n_my) of sequence b through one wave: table
 // entries are preloaded 64 at a time into a VGPR, the tiles of the next kDepth blocks are in
-// flight (`load(tile, physical_block, logical_block)`) while `process(tile, first_token_of_block)` runs on
+// flight (`load(tile, physical_block)`) while `process(tile, first_token_of_block)` runs on
 // the current one. bad is set if a table entry is outside the pool (that block's data is
 // then not read).
 template <typename TileT, int kDepth, typename L, typename F>
@@ -336,7 +294,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
     int pb = __builtin_amdgcn_readlane(tbl, i & 63);
     const bool ok = (unsigned)pb < (unsigned)a.num_blocks;
     bad |= !ok;
-    load(t, ok ? pb : 0, blk_begin + i);
+    load(t, ok ? pb : 0);
   };
 
   constexpr int NB = kDepth + 1;
@@ -359,13 +317,10 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
   }
 }
 
-// stream_tiles over the K/V pools of KV head j in the storage dtype. kNew (fused append):
-// the slot of token new_tok is read from the new K/V rows of (b, j) (load_tile_new).
-template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true, bool kNew = false,
-          typename F>
+// stream_tiles over the K/V pools of KV head j in the storage dtype.
+template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true, typename F>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
-                                              int n_my, int lane, int& bad, F&& process,
-                                              int new_tok = -1) {
+                                              int n_my, int lane, int& bad, F&& process) {
   using G_ = Geo<DT, D>;
   const int r = lane >> 4, c = lane & 15;
   const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;    // bytes between tokens
@@ -375,18 +330,9 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
   const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
   stream_tiles<Tile<DT, D>, kDepth>(
       a, b, blk_begin, n_my, lane, bad,
-      [&](Tile<DT, D>& t, int pb, int blk) {
-        const char* kb = a.k_pool + (size_t)pb * blk_stride;
-        const char* vb = a.v_pool + (size_t)pb * blk_stride;
-        if constexpr (kNew) {
-          if (blk == (new_tok >> 4)) {
-            const size_t row = ((size_t)b * a.n_kv_heads + j) * G_::kRow;
-            load_tile_new<DT, D, NT_V>(t, kb, vb, k_lane, v_lane, tok_stride, a.k_new + row,
-                                       a.v_new + row, new_tok & (kBlockTokens - 1), lane);
-            return;
-          }
-        }
-        load_tile<DT, D, NT_V>(t, kb, vb, k_lane, v_lane, tok_stride);
+      [&](Tile<DT, D>& t, int pb) {
+        load_tile<DT, D, NT_V>(t, a.k_pool + (size_t)pb * blk_stride,
+                               a.v_pool + (size_t)pb * blk_stride, k_lane, v_lane, tok_stride);
       },
       process);
 }
@@ -407,40 +353,71 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, bool used, size_
 
 // One wave: blocks [blk_begin, blk_begin + n_my) of sequence b, KV head j, into st
 // (lane-partial; finish_rows completes it). Tokens >= tok_end are masked.
-// Fused append (kAppend): the tile of the block holding token t_new = N_b - 1 (the one
-// appended by this launch) was loaded with that token's K/V from k_new / v_new; this
-// stores them from the tile into the token's pool slot (table[b][t_new / 16], t_new % 16).
-// Exactly one wave per (b, j) processes that block and no other wave of the launch reads
-// the slot, so the store needs no ordering within the launch. An out-of-range table entry
-// skips the store (the sequence's output is NaN anyway).
+// Fused append (kAppend): token t_new = N_b - 1 of sequence b is the one this launch
+// appends; its K/V rows for KV head j are k_new / v_new[b][j]. The wave whose blocks
+// include t_new's block copies the two rows into its LDS slot (1 KiB per wave) with
+// direct-to-LDS loads issued before its first tile, so the copy costs no registers and no
+// wait of its own: vector-memory loads of a wave complete in issue order, so once the wave
+// has waited for any of its tiles the rows are in LDS. When that block is processed its
+// lanes take the token's slot from LDS instead of the pool's (new_into_tile), and after
+// the stream the rows are stored into the slot (table[b][t_new / 16], t_new % 16)
+// (new_into_pool). Exactly one wave per (b, j) processes that block and no other wave of
+// the launch reads the slot, so the store needs no ordering within the launch; an
+// out-of-range table entry skips it (the sequence's output is NaN anyway).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+
 template <int DT, int D>
-__device__ __forceinline__ void store_new_slot(const DecodeArgs& a, const Tile<DT, D>& t, int b,
-                                               int j, int t_new, int lane) {
+__device__ __forceinline__ void new_rows_to_lds(const DecodeArgs& a, int b, int j, int lane,
+                                                u32x4* slot) {
+  constexpr int kL = Geo<DT, D>::kRow / 16;            // 16-byte pieces per row
+  const size_t row = ((size_t)b * a.n_kv_heads + j) * Geo<DT, D>::kRow;
+  if (lane < 2 * kL) {                                  // lane l fills slot[l]
+    const char* src = (lane < kL ? a.k_new : a.v_new) + row + 16 * (lane % kL);
+    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)slot, 16, 0, 0);
+  }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void new_into_tile(Tile<DT, D>& t, const u32x4* slot, int off,
+                                              int lane) {
   using G_ = Geo<DT, D>;
+  constexpr int kL = G_::kRow / 16;
   const int r = lane >> 4, c = lane & 15;
-  const int off = t_new & (kBlockTokens - 1);
+  // a zero that the compiler sees as depending on this tile's data: the LDS reads below
+  // come after the wait for the tile, hence after the earlier direct-to-LDS loads
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(t.k[0][0]));
+  const u32x4* sl = slot + z;
+  if (c == off) {                 // K: this lane's pieces 4 kk + r of the K row
+#pragma unroll
+    for (int kk = 0; kk < G_::kNK; ++kk) t.k[kk] = sl[4 * kk + r];
+  }
+  // V: lanes of row r = off / 4 hold token off in t.v[off % 4]; chunk c of the V row
+  const unsigned* vrow = reinterpret_cast<const unsigned*>(sl + kL) + c * G_::kVW;
+  unsigned w[G_::kVW];
+#pragma unroll
+  for (int x = 0; x < G_::kVW; ++x) w[x] = vrow[x];
+  const bool vrow_mine = r == (off >> 2);
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const bool take = vrow_mine && jj == (off & 3);
+#pragma unroll
+    for (int x = 0; x < G_::kVW; ++x) t.v[jj][x] = take ? w[x] : t.v[jj][x];
+  }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void new_into_pool(const DecodeArgs& a, const u32x4* slot, int b,
+                                              int j, int t_new, int lane) {
+  constexpr int kL = Geo<DT, D>::kRow / 16;
   const int pb = a.block_tables[(size_t)b * a.max_blocks_per_seq + (t_new >> 4)];
-  if ((unsigned)pb >= (unsigned)a.num_blocks) return;
-  const size_t dst = (((size_t)pb * kBlockTokens + off) * a.n_kv_heads + j) * G_::kRow;
-  if (c == off) {                 // K row: this lane's 16-byte pieces at 64 kk + 16 r
-    char* kd = const_cast<char*>(a.k_pool) + dst + 16 * r;
-#pragma unroll
-    for (int kk = 0; kk < G_::kNK; ++kk) *reinterpret_cast<u32x4*>(kd + 64 * kk) = t.k[kk];
-  }
-  if (r == (off >> 2)) {          // V row: this lane's chunk c of token 4r + (off & 3)
-    unsigned* vd = reinterpret_cast<unsigned*>(const_cast<char*>(a.v_pool) + dst +
-                                               (size_t)c * (G_::kEPL * G_::kE));
-    // select token (off & 3) of the lane's four with masks: a branch per token lets the
-    // compiler index the tile with a run-time value, which moves the tiles to scratch
-    const int sj = off & 3;
-#pragma unroll
-    for (int x = 0; x < G_::kVW; ++x) {
-      unsigned w = 0;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) w |= t.v[jj][x] & (jj == sj ? ~0u : 0u);
-      vd[x] = w;
-    }
-  }
+  if ((unsigned)pb >= (unsigned)a.num_blocks || lane >= 2 * kL) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the direct-to-LDS loads are done
+  const size_t dst = (((size_t)pb * kBlockTokens + (t_new & (kBlockTokens - 1))) *
+                      a.n_kv_heads + j) * Geo<DT, D>::kRow + 16 * (lane % kL);
+  char* pool = const_cast<char*>(lane < kL ? a.k_pool : a.v_pool);
+  *reinterpret_cast<u32x4*>(pool + dst) = slot[lane];
 }
 
 template <int DT, int D, int G, bool kAppend>
@@ -450,17 +427,26 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
   const int r = lane >> 4, c = lane & 15;
   u32x4 qf[Geo<DT, D>::kNK];
   load_query<DT, D>(a, c < G, (size_t)b * a.n_heads + (size_t)j * G + c, r, qf);
-  const int t_new = n_ctx - 1;                    // the appended token (kAppend)
-  stream_blocks<DT, D, Geo<DT, D>::kDepth, true, kAppend>(
-      a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
+  const int t_new = n_ctx - 1;
+  const int new_tok0 = t_new & ~(kBlockTokens - 1);
+  const bool has_new = kAppend && (new_tok0 >> 4) >= blk_begin && (new_tok0 >> 4) < blk_begin + n_my;
+  u32x4* slot = nullptr;
+  if constexpr (kAppend) {
+    __shared__ u32x4 sm_new[8][64];                     // one 1 KiB slot per wave
+    slot = sm_new[threadIdx.x >> 6];
+    if (has_new) new_rows_to_lds<DT, D>(a, b, j, lane, slot);
+  }
+  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](Tile<DT, D>& t, int tok0) {
     if constexpr (kAppend)
-      if (tok0 == (t_new & ~(kBlockTokens - 1))) store_new_slot<DT, D>(a, t, b, j, t_new, lane);
+      if (tok0 == new_tok0) new_into_tile<DT, D>(t, slot, t_new & (kBlockTokens - 1), lane);
     // only the last block of a sequence can be partial (partitions are block aligned)
     if (tok0 + kBlockTokens > tok_end)
       process_block<DT, D, G, true>(st, t, qf, tok0, tok_end, a.scale_log2, r);
     else
       process_block<DT, D, G, false>(st, t, qf, tok0, tok_end, a.scale_log2, r);
-  }, t_new);
+  });
+  if constexpr (kAppend)
+    if (has_new) new_into_pool<DT, D>(a, slot, b, j, t_new, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -917,7 +903,7 @@ __device__ __forceinline__ void attend_q(QState<DT, D>& st, int& bad, const Deco
   const char* vc = static_cast<const char*>(a.v_pool);
   stream_tiles<QTile<D>, 2>(
       a, b, blk_begin, n_my, lane, bad,
-      [&](QTile<D>& t, int pb, int) {
+      [&](QTile<D>& t, int pb) {
         const char* kb = kc + (size_t)pb * blk_stride;
         const char* vb = vc + (size_t)pb * blk_stride;
 #pragma unroll
