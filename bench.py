@@ -62,11 +62,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default 200 for the decode step, 50 otherwise)")
+                    help="timed steps (default 200; 50 for the block manager)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default 1000 for the decode step, about 0.2 s: "
-                         "the GPU's clocks settle over the first tens of milliseconds of load; "
-                         "10 otherwise)")
+                    help="untimed steps first (default 1000, a fraction of a second: step "
+                         "times fall by ~1.5%% over the first tens of milliseconds of load as "
+                         "the GPU's clocks settle; 10 for the block manager)")
     ap.add_argument("--config", type=int, default=2, help="workload id 1..5 (default 2)")
     ap.add_argument("--partition", type=int, default=0,
                     help="tokens per KV partition; 0 = the library's balanced split")
@@ -93,11 +93,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
     args = ap.parse_args()
-    decode = args.component == "decode"
+    gpu_steps = args.component != "block-manager"
     if args.steps is None:
-        args.steps = 200 if decode else 50
+        args.steps = 200 if gpu_steps else 50
     if args.warmup is None:
-        args.warmup = 1000 if decode else 10
+        args.warmup = 1000 if gpu_steps else 10
     return args
 
 

@@ -20,9 +20,14 @@ ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled on purpose: every fp32 operation in the kernels
 # is written as scalar float code and must lower to unpacked VALU instructions.
+# Matrix-core accumulators are kept in ordinary vector registers (the MFMA VGPR form):
+# the kernels that accumulate P.V on the matrix cores (multi-query, quantized, shared-
+# prefix pass) otherwise shuttle them through the accumulation registers around every
+# rescale, which costs 3-10% in those kernels; the other kernels compile the same.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-shared", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
 ]
 
