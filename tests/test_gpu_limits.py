@@ -49,9 +49,11 @@ def _sampled(wl, n, seed):
     return [(b, h) for b in seqs for h in range(wl.spec.n_heads)]
 
 
-def test_pools_beyond_4gib():
+@pytest.mark.parametrize("fused", [False, True])
+def test_pools_beyond_4gib(fused):
     """The small GQA workload moved to the top of a 4.6 GB pool: every block offset exceeds
-    2^32 bytes; append and decode must match the oracle on the original placement."""
+    2^32 bytes; append and decode (two launches, or the fused step) must match the oracle
+    on the original placement."""
     wl = wlm.make_workload(3, small=True)
     nb, bs, Hkv, d = wl.k_pool.shape
     block_bytes = bs * Hkv * d * 2
@@ -66,10 +68,14 @@ def test_pools_beyond_4gib():
     tables = t["block_tables"].clone()
     used = tables >= 0
     tables[used] += base
-    pkv.pkv_kv_append(kbig, vbig, t["k_new"], t["v_new"], tables, t["positions"])
     out = torch.empty_like(t["q"])
-    pkv.pkv_paged_decode_attention(out, t["q"], kbig, vbig, tables, t["context_lens"],
-                                   wl.max_context_len, wl.scale)
+    if fused:
+        pkv.pkv_paged_decode_step(out, t["q"], kbig, vbig, t["k_new"], t["v_new"], tables,
+                                  t["context_lens"], wl.max_context_len, wl.scale)
+    else:
+        pkv.pkv_kv_append(kbig, vbig, t["k_new"], t["v_new"], tables, t["positions"])
+        pkv.pkv_paged_decode_attention(out, t["q"], kbig, vbig, tables, t["context_lens"],
+                                       wl.max_context_len, wl.scale)
     torch.cuda.synchronize()
     kp, vp = orc.kv_append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.block_tables,
                            wl.positions, 16)
