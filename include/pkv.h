@@ -233,6 +233,32 @@ size_t pkv_multi_query_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t 
                                        int32_t max_context_len, int32_t partition_tokens);
 
 /*
+ * pkv_paged_multi_query_step - pkv_kv_append_tokens followed by
+ * pkv_paged_multi_query_attention, in one launch. Source: the q_len new tokens' K/V enter
+ * the cache before they are attended to ("09-inference-optimization", KV Cache, with
+ * seq_len > 1 new tokens; "LLM推理与服务：面试问题与推荐回答" Q9 speculative verification).
+ * The appended tokens of sequence b are tokens context_lens[b] - q_len .. context_lens[b] - 1
+ * (positions are implied); k_new, v_new [num_seqs, q_len, n_kv_heads, d_head] in dtype, row
+ * i being token context_lens[b] - q_len + i. The waves that attend over the blocks holding
+ * those tokens take their K/V straight from k_new / v_new and write them into the pool
+ * slots, so the pools afterwards equal those of the two separate calls and `out` equals
+ * their result (same arithmetic); q_len = 1 is pkv_paged_decode_step. Sequences whose
+ * length is invalid get NaN outputs and no append; a table entry outside the pool skips the
+ * writes into that block (NaN output). k_pool, v_pool are written; the other arguments are
+ * those of pkv_paged_multi_query_attention (workspace size from
+ * pkv_multi_query_workspace_bytes).
+ */
+int32_t pkv_paged_multi_query_step(void* out, const void* q, void* k_pool, void* v_pool,
+                                   const void* k_new, const void* v_new,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t q_len, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, int32_t max_context_len,
+                                   int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+                                   int32_t d_head, float scale, int32_t partition_tokens,
+                                   int32_t dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/*
  * pkv_paged_decode_attention_shared_prefix - pkv_paged_decode_attention for a batch in
  * which groups of sequences share the first blocks of their tables (a common prompt,
  * parallel sampling, beam search), reading every shared block once per group.

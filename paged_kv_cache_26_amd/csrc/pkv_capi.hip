@@ -155,7 +155,7 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
                          overlaps(out, out_bytes, v_scales, scale_bytes)))
     return PKV_ERR_ALIAS;
   if (fused_append) {
-    const size_t new_bytes = (size_t)num_seqs * n_kv_heads * d_head * eb;
+    const size_t new_bytes = (size_t)num_seqs * q_len * n_kv_heads * d_head * eb;
     if (overlaps(out, out_bytes, k_new, new_bytes) || overlaps(out, out_bytes, v_new, new_bytes) ||
         overlaps(k_new, new_bytes, k_pool, pool_bytes) || overlaps(k_new, new_bytes, v_pool, pool_bytes) ||
         overlaps(v_new, new_bytes, k_pool, pool_bytes) || overlaps(v_new, new_bytes, v_pool, pool_bytes) ||
@@ -423,6 +423,21 @@ int32_t pkv_paged_multi_query_attention(void* out, const void* q, const void* k_
                      max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
                      n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
                      workspace_bytes, stream);
+}
+
+int32_t pkv_paged_multi_query_step(void* out, const void* q, void* k_pool, void* v_pool,
+                                   const void* k_new, const void* v_new,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t num_seqs, int32_t q_len, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, int32_t max_context_len,
+                                   int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+                                   int32_t d_head, float scale, int32_t partition_tokens,
+                                   int32_t dtype, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, q_len,
+                     max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
+                     n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
+                     workspace_bytes, stream, 0, nullptr, nullptr, k_new, v_new, true);
 }
 
 size_t pkv_shared_prefix_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_kv_heads,

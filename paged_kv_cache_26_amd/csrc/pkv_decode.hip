@@ -591,7 +591,88 @@ __device__ __forceinline__ size_t mq_row(const DecodeArgs& a, int b, int j, int 
   return ((size_t)b * a.q_len + i) * a.n_heads + (size_t)j * G + h;
 }
 
+// Fused append of q_len > 1 tokens (kAppend): tokens t0n = N_b - q_len .. N_b - 1 of
+// sequence b are appended by this launch; row i of k_new / v_new[b][i][j] is token
+// t0n + i's K / V for KV head j. As for one token (attend with kAppend), a wave whose
+// blocks hold any of them copies all q_len rows into its LDS slot with direct-to-LDS loads
+// before its first tile, takes the new tokens' slots of a tile from LDS, and after the
+// stream stores the rows of the tokens in its own blocks into their pool slots. The (at
+// most two) blocks holding new tokens may belong to different waves; each writes only its
+// own blocks, which no other wave of the launch reads.
 template <int DT, int D, int G>
+struct NewRowsMq {
+  static constexpr int kL = Geo<DT, D>::kRow / 16;      // 16-byte pieces per row
+  static constexpr int kRowsMax = 16 / G;               // q_len <= 16 / G
+  static constexpr int kVOff = kRowsMax * kL;           // V rows follow the K rows
+  static constexpr int kPieces = 2 * kVOff;
+};
+
+template <int DT, int D, int G>
+__device__ __forceinline__ void new_rows_to_lds_mq(const DecodeArgs& a, int b, int j, int lane,
+                                                   u32x4* slot) {
+  using N_ = NewRowsMq<DT, D, G>;
+  const int n = a.q_len * N_::kL;                       // pieces of the K (or V) rows
+  for (int x0 = 0; x0 < n; x0 += 64) {
+    const int x = x0 + lane, i = x / N_::kL, pc = x - i * N_::kL;
+    const size_t row = (((size_t)b * a.q_len + i) * a.n_kv_heads + j) * Geo<DT, D>::kRow;
+    if (x < n) {
+      __builtin_amdgcn_global_load_lds((global_void_t*)(a.k_new + row + 16 * pc),
+                                       (lds_void_t*)(slot + x0), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_void_t*)(a.v_new + row + 16 * pc),
+                                       (lds_void_t*)(slot + N_::kVOff + x0), 16, 0, 0);
+    }
+  }
+}
+
+template <int DT, int D, int G>
+__device__ __forceinline__ void new_into_tile_mq(Tile<DT, D>& t, const u32x4* slot, int tok0,
+                                                 int t0n, int q_len, int lane) {
+  using G_ = Geo<DT, D>;
+  using N_ = NewRowsMq<DT, D, G>;
+  const int r = lane >> 4, c = lane & 15;
+  int z;                                                // orders the LDS reads after the tile
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(t.k[0][0]));
+  const u32x4* sl = slot + z;
+  const int tk = tok0 + c - t0n;                        // new-token row of this lane's K
+  if ((unsigned)tk < (unsigned)q_len) {
+#pragma unroll
+    for (int kk = 0; kk < G_::kNK; ++kk) t.k[kk] = sl[tk * N_::kL + 4 * kk + r];
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {                      // token 4r + jj, chunk c of its V row
+    const int tv = tok0 + 4 * r + jj - t0n;
+    const bool take = (unsigned)tv < (unsigned)q_len;
+    const unsigned* vrow =
+        reinterpret_cast<const unsigned*>(sl + N_::kVOff + (take ? tv : 0) * N_::kL) + c * G_::kVW;
+#pragma unroll
+    for (int x = 0; x < G_::kVW; ++x) {
+      const unsigned w = vrow[x];
+      t.v[jj][x] = take ? w : t.v[jj][x];
+    }
+  }
+}
+
+template <int DT, int D, int G>
+__device__ __forceinline__ void new_into_pool_mq(const DecodeArgs& a, const u32x4* slot, int b,
+                                                 int j, int t0n, int blk_begin, int n_my,
+                                                 int lane) {
+  using N_ = NewRowsMq<DT, D, G>;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the direct-to-LDS loads are done
+  const int n = a.q_len * N_::kL;
+  for (int x = lane; x < n; x += 64) {
+    const int i = x / N_::kL, pc = x - i * N_::kL;
+    const int tok = t0n + i, blk = tok >> 4;
+    if (blk < blk_begin || blk >= blk_begin + n_my) continue;   // another wave's block
+    const int pb = a.block_tables[(size_t)b * a.max_blocks_per_seq + blk];
+    if ((unsigned)pb >= (unsigned)a.num_blocks) continue;
+    const size_t dst = (((size_t)pb * kBlockTokens + (tok & (kBlockTokens - 1))) * a.n_kv_heads +
+                        j) * Geo<DT, D>::kRow + 16 * pc;
+    *reinterpret_cast<u32x4*>(const_cast<char*>(a.k_pool) + dst) = slot[x];
+    *reinterpret_cast<u32x4*>(const_cast<char*>(a.v_pool) + dst) = slot[N_::kVOff + x];
+  }
+}
+
+template <int DT, int D, int G, bool kAppend>
 __device__ __forceinline__ void attend_mq(MqState<DT, D>& st, int& bad, const DecodeArgs& a,
                                           int b, int j, int blk_begin, int n_my, int tok_end,
                                           int n_ctx, int lane) {
@@ -602,12 +683,24 @@ __device__ __forceinline__ void attend_mq(MqState<DT, D>& st, int& bad, const De
   const int first_visible_end = n_ctx - a.q_len + 1;     // limit of query 0
   const int lim = c < C ? min(tok_end, first_visible_end + c / G) : tok_end;
   const int lim_min = min(tok_end, first_visible_end);
-  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](const Tile<DT, D>& t, int tok0) {
+  const int t0n = n_ctx - a.q_len;                      // first appended token (kAppend)
+  const bool has_new = kAppend && (t0n >> 4) < blk_begin + n_my && ((n_ctx - 1) >> 4) >= blk_begin;
+  u32x4* slot = nullptr;
+  if constexpr (kAppend) {
+    __shared__ u32x4 sm_new[8][NewRowsMq<DT, D, G>::kPieces];   // one slot per wave
+    slot = sm_new[threadIdx.x >> 6];
+    if (has_new) new_rows_to_lds_mq<DT, D, G>(a, b, j, lane, slot);
+  }
+  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](Tile<DT, D>& t, int tok0) {
+    if constexpr (kAppend)
+      if (has_new && tok0 + kBlockTokens > t0n) new_into_tile_mq<DT, D, G>(t, slot, tok0, t0n, a.q_len, lane);
     if (tok0 + kBlockTokens > lim_min)
       process_block_mq<DT, D, true>(st, t, qf, tok0, tok_end, lim, lim_min, a.scale_log2, r);
     else
       process_block_mq<DT, D, false>(st, t, qf, tok0, tok_end, lim, lim_min, a.scale_log2, r);
   });
+  if constexpr (kAppend)
+    if (has_new) new_into_pool_mq<DT, D, G>(a, slot, b, j, t0n, blk_begin, n_my, lane);
 }
 
 template <int DT, int D, int G>
@@ -1034,7 +1127,8 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, i
       write_record<DT, D, G>(a, st, bad, lane, rec);
   } else {
     MqState<DT, D> st;
-    attend_mq<DT, D, G>(st, bad, a, b, j, blk_begin, n_my, tok_end, n_ctx, lane);
+    attend_mq<DT, D, G, MODE == kModeMultiAppend>(st, bad, a, b, j, blk_begin, n_my, tok_end,
+                                                n_ctx, lane);
     st.l += __shfl_xor(st.l, 16);
     st.l += __shfl_xor(st.l, 32);
     if (whole)
@@ -1443,7 +1537,8 @@ hipError_t launch_mq(const DecodeArgs& a, hipStream_t stream) {
   if (a.q_len == 1)
     return a.k_new ? launch_typed<DT, D, G, NW, kModeSingleAppend>(a, stream)
                    : launch_typed<DT, D, G, NW, kModeSingle>(a, stream);
-  return launch_typed<DT, D, G, NW, kModeMulti>(a, stream);
+  return a.k_new ? launch_typed<DT, D, G, NW, kModeMultiAppend>(a, stream)
+                 : launch_typed<DT, D, G, NW, kModeMulti>(a, stream);
 }
 
 template <int DT, int D, int G>

@@ -25,6 +25,7 @@ constexpr int kModeMulti = 1;       // q_len queries per sequence, P.V on the ma
 constexpr int kModeQuantInt8 = 2;   // one query, INT8 codes + (s, z) per token and KV head
 constexpr int kModeQuantFp8 = 3;    // one query, E4M3 codes + (s, 0) per token and KV head
 constexpr int kModeSingleAppend = 4; // kModeSingle that also appends the new token (k_new)
+constexpr int kModeMultiAppend = 5;  // kModeMulti that also appends the q_len new tokens
 
 // Waves per decode workgroup (one KV head each) used with this many KV heads. The
 // launcher may use fewer (4) for kernels that do not fit 256 registers per lane; this is

@@ -75,6 +75,9 @@ _SIGNATURES = {
     "pkv_paged_decode_step": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 8 + [ctypes.c_float, _c_i32,
                                                                      _c_i32, _c_ptr, _c_size,
                                                                      _c_ptr]),
+    "pkv_paged_multi_query_step": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 9 + [ctypes.c_float, _c_i32,
+                                                                          _c_i32, _c_ptr,
+                                                                          _c_size, _c_ptr]),
     "pkv_stream_read": (_c_i32, [_c_ptr, _c_size, _c_ptr, _c_size, _c_i32, _c_ptr]),
     "pkv_find_shared_prefixes": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr,
                                           _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
@@ -277,6 +280,37 @@ def pkv_paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, contex
         _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_paged_multi_query_attention")
+    return out
+
+
+def pkv_paged_multi_query_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                               max_context_len: int, scale: float | None = None,
+                               partition_tokens: int = 0, workspace=None, stream=None):
+    """pkv_kv_append_tokens (tokens context_lens[b] - q_len ..) and
+    pkv_paged_multi_query_attention in one launch; k_new/v_new [B, q_len, H_kv, d].
+    Returns out."""
+    lib = load_library()
+    _check_device(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens)
+    _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype ==
+             k_new.dtype == v_new.dtype, "q, out, pools and new rows must share a dtype")
+    _require(q.dim() == 4 and out.shape == q.shape, "q/out must be [B, q_len, H, d]")
+    B, ql, H, d = q.shape
+    _require(k_new.shape == v_new.shape and k_new.shape == (B, ql, k_pool.shape[2], d),
+             "k_new/v_new must be [B, q_len, H_kv, d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = pkv_multi_query_workspace_bytes(B, ql, H, k_pool.shape[2], d, max_context_len,
+                                           partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.pkv_paged_multi_query_step(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+        _ptr(block_tables), _ptr(context_lens), B, ql, block_tables.shape[1], k_pool.shape[0],
+        int(max_context_len), k_pool.shape[1], H, k_pool.shape[2], d, float(scale),
+        int(partition_tokens), _DTYPE_CODE[q.dtype], _ptr(workspace), ws_bytes, _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_paged_multi_query_step")
     return out
 
 

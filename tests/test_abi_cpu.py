@@ -215,3 +215,17 @@ def test_fused_step_rejects_bad_arguments_on_host(lib):
         args[idx] = val
         assert f(*args) == code, (idx, val)
     assert f(*good) == -9                     # the balanced split needs its workspace
+
+
+def test_multi_query_step_rejects_bad_arguments_on_host(lib):
+    f = lib.pkv_paged_multi_query_step
+    # out, q, k_pool, v_pool, k_new, v_new, tables, lens, B, q_len, maxb, nb, maxctx, bs, H,
+    # Hkv, d, scale, partition, dtype, workspace, bytes, stream
+    good = [0x1000000, 0x2000000, 0x10000000, 0x20000000, 0x3000000, 0x4000000, 0x30000,
+            0x40000, 4, 4, 64, 64, 700, 16, 32, 8, 128, 0.1, 0, 2, 0, 0, None]
+    for idx, val, code in [(4, 0, -1), (5, 0, -1), (4, 0x3000008, -11), (4, 0x1000000, -12),
+                           (5, 0x10000000, -12), (19, 3, -3), (9, 0, -17), (9, 5, -17)]:
+        args = list(good)
+        args[idx] = val
+        assert f(*args) == code, (idx, val)
+    assert f(*good) == -9                     # the balanced split needs its workspace
