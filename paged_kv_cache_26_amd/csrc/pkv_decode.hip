@@ -1381,6 +1381,96 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 }
 
 
+// merge_kernel for many rows with few records each: one wave per output row, four rows
+// per workgroup. The wave walks the row's records in order, first for the maximum m, then
+// for l and O (lane: D / 64 consecutive elements): two rounds of loads and no barrier,
+// and a quarter of the workgroups. Used when the launch has at least kMergeRowsWave rows
+// (a batch of many sequences, or q_len > 1, cuts each sequence into few segments); a few
+// long sequences, each cut into many segments, keep merge_kernel's four waves per row.
+template <int DT, int D, int NW>
+__global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
+  constexpr int EL = D / 64;                   // output elements per lane
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // (b * q_len + i) * n_heads + h
+  const int per_seq = a.q_len * a.n_heads;
+  if (row >= a.num_seqs * per_seq) return;     // no barrier in this kernel
+  const int b = row / per_seq;
+  const int i = (row - b * per_seq) / a.n_heads;
+  const int h = row - b * per_seq - i * a.n_heads;
+  const int n_ctx = a.context_lens[b];
+  if (!usable(a, b, n_ctx)) return;            // decode wrote NaN
+
+  size_t base, stride, pbase = 0;
+  int n_rec, n_pre = 0;
+  if (a.split) {
+    const int B = a.num_seqs;
+    const int G = a.n_heads / a.n_kv_heads;
+    const int C = G * a.q_len;
+    const int j = h / G, hh = h - j * G;
+    const int hg = j / NW, wv = j - hg * NW;
+    const int HG = (a.n_kv_heads + NW - 1) / NW;
+    const int T1 = a.ws_prefix[B];
+    const long long T = (long long)T1 * HG;
+    const long long W = min((long long)a.split_workgroups, (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
+    const int nb = a.ws_prefix[b + 1] - a.ws_prefix[b];
+    const long long U = (long long)hg * T1 + a.ws_prefix[b];
+    // workgroup owning unit x: the largest w with w*T/W <= x
+    const long long first = ((U + 1) * W - 1) / T;
+    const long long last = ((U + nb) * W - 1) / T;
+    const int grp = a.seq_group ? a.seq_group[b] : -1;
+    if (first == last && grp < 0) return;                   // decode wrote the output
+    n_rec = (int)(last - first + 1);
+    base = ((size_t)(first + (long long)hg * B + b) * NW + wv) * C + (size_t)i * G + hh;
+    stride = (size_t)NW * C;
+    if (grp >= 0) {
+      const int sb = a.group_blocks[grp];                   // <= max_blocks_per_seq here
+      int nan_row = 0;
+      if (sb > a.max_shared_blocks) {
+        nan_row = 1;
+      } else {
+        n_pre = (sb * kBlockTokens + kPrefixPartition - 1) / kPrefixPartition;
+        pbase = ((size_t)b * a.n_heads + h) * a.prefix_parts;
+        for (int p = lane; p < n_pre; p += 64) nan_row |= a.ws_flags[(size_t)b * a.prefix_parts + p];
+      }
+      // the group broke its promise (see prefix_kernel): NaN row
+      if (__any(nan_row)) {
+        for (int x = lane; x < D; x += 64) store_elem<DT>(a.out, (size_t)row * D + x, __builtin_nanf(""));
+        return;
+      }
+    }
+  } else {
+    n_rec = (n_ctx + a.partition_tokens - 1) / a.partition_tokens;
+    if (n_rec <= 1) return;                                 // decode wrote the output
+    base = (size_t)row * a.max_partitions;
+    stride = 1;
+  }
+
+  float M = -INFINITY;
+#pragma unroll 4
+  for (int k = 0; k < n_rec; ++k) M = fmaxf(M, a.ws_m[base + k * stride]);
+  for (int k = 0; k < n_pre; ++k) M = fmaxf(M, a.ws_pm[pbase + k]);
+  float L = 0.f, acc[EL] = {};
+#pragma unroll 4
+  for (int k = 0; k < n_rec; ++k) {
+    const size_t r = base + k * stride;
+    const float f = exp2_fast(a.ws_m[r] - M);
+    L = fmaf(a.ws_l[r], f, L);
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = fmaf(f, a.ws_o[r * D + EL * lane + e], acc[e]);
+  }
+  for (int k = 0; k < n_pre; ++k) {
+    const size_t r = pbase + k;
+    const float f = exp2_fast(a.ws_pm[r] - M);
+    L = fmaf(a.ws_pl[r], f, L);
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] = fmaf(f, a.ws_po[r * D + EL * lane + e], acc[e]);
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < EL; ++e) store_elem<DT>(a.out, (size_t)row * D + EL * lane + e, acc[e] * inv);
+}
+
+
 // Shared-prefix pass. Workgroup = 4 waves on KV head j of prefix partition p
 // (kPrefixPartition tokens) of group g, column set cs; wave w owns the 16 columns
 // k = cs * 64 + 16 * w + c (lane column c), column k being the pair (member m = k / G,
@@ -1527,8 +1617,11 @@ hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !need_merge) return e;
-  hipLaunchKernelGGL((merge_kernel<DT, D, NW>), dim3(a.num_seqs * a.q_len * a.n_heads), dim3(256), 0,
-                     stream, a);
+  const int rows = a.num_seqs * a.q_len * a.n_heads;
+  if (rows >= kMergeRowsWave)
+    hipLaunchKernelGGL((merge_rows_kernel<DT, D, NW>), dim3((rows + 3) / 4), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<DT, D, NW>), dim3(rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

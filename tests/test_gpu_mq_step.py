@@ -136,3 +136,14 @@ def test_bad_entries_skip_the_append_and_give_nan():
             skipped = b == 4 or (b == 2 and p // 16 == (n2 - 1) // 16)
             want = prev[blk, off] if skipped else kp[blk, off]
             assert np.array_equal(after[blk, off], want), (b, i)
+
+
+def test_many_rows_use_the_wave_per_row_merge():
+    """20 sequences x 4 new tokens x 32 heads = 2560 output rows: the merge runs one wave
+    per row (from 2048 rows on); the result must still match the oracle."""
+    wl = mq_workload(4, B=20, lo=600, hi=2500, seed=21)
+    out, t = check_against_separate(wl, 0)
+    kp, vp = oracle_pools(wl)
+    ref = orc.paged_multi_query_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                          wl.scale, "bf16")
+    assert_close(out.double().cpu().numpy(), ref, "bf16", "many rows")
