@@ -1196,31 +1196,49 @@ __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
 template <int DT, int D, int G, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW;
+  constexpr int kScanChunks = kSplitMaxSeqs / 64;
+  static_assert(kScanChunks <= 64, "one lane per chunk of 64 sequences");
   __shared__ int sm_pref[kSplitMaxSeqs + 1];   // blocks of sequences before b
-  __shared__ int sm_scan[kThreads];
+  __shared__ int sm_chunk[kScanChunks];         // blocks of each chunk of 64 sequences
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = a.num_seqs;
 
   // Exclusive prefix sum of the block counts (sequences with an invalid length count 0).
-  const int chunk = (B + kThreads - 1) / kThreads;
-  const int s0 = min(B, tid * chunk), s1 = min(B, s0 + chunk);
-  int run = 0;
-  for (int s = s0; s < s1; ++s) {
-    const int n = a.context_lens[s];
-    sm_pref[s] = run;
-    run += usable(a, s, n) ? (n + kBlockTokens - 1) / kBlockTokens - shared_blocks_of(a, s, n) : 0;
+  // Wave v scans chunks v, v + NW, ... of 64 sequences across its lanes; after one barrier
+  // every wave scans the chunk totals and adds each chunk's offset: two barriers in all.
+  const int n_chunks = (B + 63) / 64;
+  auto inclusive_scan = [&](int x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off);
+      if (lane >= off) x += y;
+    }
+    return x;
+  };
+  for (int c = wave; c < n_chunks; c += NW) {
+    const int s = c * 64 + lane;
+    int nb = 0;
+    if (s < B) {
+      const int n = a.context_lens[s];
+      nb = usable(a, s, n) ? (n + kBlockTokens - 1) / kBlockTokens - shared_blocks_of(a, s, n) : 0;
+    }
+    const int incl = inclusive_scan(nb);
+    if (s < B) sm_pref[s] = incl - nb;
+    if (lane == 63) sm_chunk[c] = incl;
   }
-  sm_scan[tid] = run;
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int v = tid >= off ? sm_scan[tid - off] : 0;
-    __syncthreads();
-    sm_scan[tid] += v;
-    __syncthreads();
+  {
+    const int tot = lane < n_chunks ? sm_chunk[lane] : 0;
+    const int incl = inclusive_scan(tot);
+    const int excl = incl - tot;                // blocks of the chunks before chunk `lane`
+    for (int c = wave; c < n_chunks; c += NW) {
+      const int off = __shfl(excl, c);
+      const int s = c * 64 + lane;
+      if (s < B) sm_pref[s] += off;
+    }
+    const int total = __shfl(incl, 63);
+    if (tid == 0) sm_pref[B] = total;
   }
-  const int before = tid > 0 ? sm_scan[tid - 1] : 0;
-  for (int s = s0; s < s1; ++s) sm_pref[s] += before;
-  if (tid == kThreads - 1) sm_pref[B] = sm_scan[kThreads - 1];
   __syncthreads();
 
   const int w = blockIdx.x;
