@@ -32,7 +32,8 @@
 //   * P.V on the vector ALU in fp32: lane (r, c) loads d_head/16 consecutive elements
 //     (chunk c) of token 4r + jj for jj = 0..3, and gets each head's probability for that
 //     token from lane (r, h) with a DPP row broadcast.
-// K and V are prefetched kDepth blocks ahead into registers. V rows are read with the
+// K and V are prefetched into registers one block ahead (stream_tiles_pipelined for the
+// single-query kernels, stream_tiles for the others). V rows are read with the
 // non-temporal hint (each byte is used once); K keeps the default policy because two
 // consecutive loads of a wave share each 128-byte line.
 
@@ -317,10 +318,79 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
   }
 }
 
+// The same stream with a branch-free steady-state loop: every iteration loads one table
+// entry (for the block it fetches next time) and one tile, so the compiler's wait analysis
+// sees the same sequence of loads on every path and waits for exactly the tile being
+// processed. In stream_tiles the table refill every 64 blocks and the fetches skipped in the
+// last iterations make it wait for every outstanding load before each fetch; there the
+// wave keeps one block in flight, fetched a whole block ahead. With kDepth = 1 this loop
+// keeps one block in flight too, but without the drains and with the last blocks in a
+// loop of their own; the single-query kernels run faster with it (the multi-query and
+// quantized ones do not, and keep stream_tiles). `begin()` runs once, right after the
+// first table entry's load is issued.
+template <typename TileT, int kDepth, typename L, typename F, typename S>
+__device__ __forceinline__ void stream_tiles_pipelined(const DecodeArgs& a, int b, int blk_begin,
+                                                       int n_my, int& bad, L&& load,
+                                                       F&& process, S&& begin) {
+  const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_begin;
+  auto entry = [&](int i) { return trow[min(i, n_my - 1)]; };   // same address in all lanes
+  auto fetch = [&](TileT& t, int pb) {
+    pb = __builtin_amdgcn_readfirstlane(pb);
+    const bool ok = (unsigned)pb < (unsigned)a.num_blocks;
+    bad |= !ok;
+    load(t, ok ? pb : 0);
+  };
+
+  constexpr int NB = kDepth + 1;
+  TileT tt[NB];
+  // Loads in the order of the loop body (entry of block d + 1, then tile d), so the loop is
+  // entered with the same outstanding loads as it repeats with; a segment shorter than
+  // kDepth blocks loads its last block again instead of skipping the load.
+  int e_next = entry(0);                    // table entry of the next block to fetch
+  begin();
+#pragma unroll
+  for (int d0 = 0; d0 < kDepth; ++d0) {
+    const int pb = e_next;
+    e_next = entry(d0 + 1);
+    fetch(tt[d0], pb);
+  }
+  const int n_fetching = n_my - kDepth;     // iterations i < n_fetching fetch block i + kDepth
+  int i0 = 0;
+  for (; i0 + NB <= n_fetching; i0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      const int pb = e_next;
+      e_next = entry(i + kDepth + 1);
+      fetch(tt[(u + kDepth) % NB], pb);
+      process(tt[u], (blk_begin + i) * kBlockTokens);
+    }
+  }
+  for (; i0 < n_my; i0 += NB) {              // at most NB + kDepth - 1 blocks
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      if (i >= n_my) break;
+      if (i < n_fetching) {
+        const int pb = e_next;
+        e_next = entry(i + kDepth + 1);
+        fetch(tt[(u + kDepth) % NB], pb);
+      }
+      process(tt[u], (blk_begin + i) * kBlockTokens);
+    }
+  }
+}
+
 // stream_tiles over the K/V pools of KV head j in the storage dtype.
-template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true, typename F>
+struct NoBegin {
+  __device__ void operator()() const {}
+};
+
+template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true,
+          bool kPipelined = false, typename F, typename S = NoBegin>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
-                                              int n_my, int lane, int& bad, F&& process) {
+                                              int n_my, int lane, int& bad, F&& process,
+                                              S&& begin = S{}) {
   using G_ = Geo<DT, D>;
   const int r = lane >> 4, c = lane & 15;
   const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;    // bytes between tokens
@@ -328,13 +398,16 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
   const uint32_t head_off = (uint32_t)j * G_::kRow;
   const uint32_t k_lane = head_off + c * tok_stride + 16 * r;
   const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * (G_::kEPL * G_::kE);
-  stream_tiles<Tile<DT, D>, kDepth>(
-      a, b, blk_begin, n_my, lane, bad,
-      [&](Tile<DT, D>& t, int pb) {
-        load_tile<DT, D, NT_V>(t, a.k_pool + (size_t)pb * blk_stride,
-                               a.v_pool + (size_t)pb * blk_stride, k_lane, v_lane, tok_stride);
-      },
-      process);
+  auto load = [&](Tile<DT, D>& t, int pb) {
+    load_tile<DT, D, NT_V>(t, a.k_pool + (size_t)pb * blk_stride,
+                           a.v_pool + (size_t)pb * blk_stride, k_lane, v_lane, tok_stride);
+  };
+  if constexpr (kPipelined) {
+    stream_tiles_pipelined<Tile<DT, D>, kDepth>(a, b, blk_begin, n_my, bad, load, process, begin);
+  } else {
+    begin();
+    stream_tiles<Tile<DT, D>, kDepth>(a, b, blk_begin, n_my, lane, bad, load, process);
+  }
 }
 
 // Query fragments (MFMA B operand) for lane column c: 16-byte slices at 64*kk + 16*r of
@@ -355,27 +428,26 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, bool used, size_
 // (lane-partial; finish_rows completes it). Tokens >= tok_end are masked.
 // Fused append (kAppend): token t_new = N_b - 1 of sequence b is the one this launch
 // appends; its K/V rows for KV head j are k_new / v_new[b][j]. The wave whose blocks
-// include t_new's block copies the two rows into its LDS slot (1 KiB per wave) with
-// direct-to-LDS loads issued before its first tile, so the copy costs no registers and no
-// wait of its own: vector-memory loads of a wave complete in issue order, so once the wave
-// has waited for any of its tiles the rows are in LDS. When that block is processed its
-// lanes take the token's slot from LDS instead of the pool's (new_into_tile), and after
-// the stream the rows are stored into the slot (table[b][t_new / 16], t_new % 16)
-// (new_into_pool). Exactly one wave per (b, j) processes that block and no other wave of
-// the launch reads the slot, so the store needs no ordering within the launch; an
-// out-of-range table entry skips it (the sequence's output is NaN anyway).
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void global_void_t;
-
+// include t_new's block loads the two rows into registers (one 16-byte piece per lane)
+// before its stream and writes them to its LDS slot (1 KiB per wave) in the stream's begin
+// hook, while the first table entry is in flight; the registers are dead before the block
+// loop. When that block is processed its lanes take the token's slot from LDS instead of
+// the pool's (new_into_tile), and after the stream the rows are stored into the slot
+// (table[b][t_new / 16], t_new % 16) (new_into_pool). Exactly one wave per (b, j)
+// processes that block and no other wave of the launch reads the slot, so the store needs
+// no ordering within the launch; an out-of-range table entry skips it (the sequence's
+// output is NaN anyway). (Direct-to-LDS loads, which the multi-query append uses, would
+// make the compiler drain every outstanding load at each block of the pipelined stream:
+// it treats each LDS access in the loop as possibly reading what they write.)
 template <int DT, int D>
-__device__ __forceinline__ void new_rows_to_lds(const DecodeArgs& a, int b, int j, int lane,
-                                                u32x4* slot) {
+__device__ __forceinline__ u32x4 new_rows_load(const DecodeArgs& a, int b, int j, int lane) {
   constexpr int kL = Geo<DT, D>::kRow / 16;            // 16-byte pieces per row
   const size_t row = ((size_t)b * a.n_kv_heads + j) * Geo<DT, D>::kRow;
-  if (lane < 2 * kL) {                                  // lane l fills slot[l]
-    const char* src = (lane < kL ? a.k_new : a.v_new) + row + 16 * (lane % kL);
-    __builtin_amdgcn_global_load_lds((global_void_t*)src, (lds_void_t*)slot, 16, 0, 0);
-  }
+  u32x4 piece = {0u, 0u, 0u, 0u};
+  if (lane < 2 * kL)                                    // lane l holds slot[l]
+    piece = *reinterpret_cast<const u32x4*>((lane < kL ? a.k_new : a.v_new) + row +
+                                            16 * (lane % kL));
+  return piece;
 }
 
 template <int DT, int D>
@@ -384,11 +456,7 @@ __device__ __forceinline__ void new_into_tile(Tile<DT, D>& t, const u32x4* slot,
   using G_ = Geo<DT, D>;
   constexpr int kL = G_::kRow / 16;
   const int r = lane >> 4, c = lane & 15;
-  // a zero that the compiler sees as depending on this tile's data: the LDS reads below
-  // come after the wait for the tile, hence after the earlier direct-to-LDS loads
-  int z;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(t.k[0][0]));
-  const u32x4* sl = slot + z;
+  const u32x4* sl = slot;         // written by this wave's begin hook
   if (c == off) {                 // K: this lane's pieces 4 kk + r of the K row
 #pragma unroll
     for (int kk = 0; kk < G_::kNK; ++kk) t.k[kk] = sl[4 * kk + r];
@@ -413,7 +481,6 @@ __device__ __forceinline__ void new_into_pool(const DecodeArgs& a, const u32x4* 
   constexpr int kL = Geo<DT, D>::kRow / 16;
   const int pb = a.block_tables[(size_t)b * a.max_blocks_per_seq + (t_new >> 4)];
   if ((unsigned)pb >= (unsigned)a.num_blocks || lane >= 2 * kL) return;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");     // the direct-to-LDS loads are done
   const size_t dst = (((size_t)pb * kBlockTokens + (t_new & (kBlockTokens - 1))) *
                       a.n_kv_heads + j) * Geo<DT, D>::kRow + 16 * (lane % kL);
   char* pool = const_cast<char*>(lane < kL ? a.k_pool : a.v_pool);
@@ -431,12 +498,15 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
   const int new_tok0 = t_new & ~(kBlockTokens - 1);
   const bool has_new = kAppend && (new_tok0 >> 4) >= blk_begin && (new_tok0 >> 4) < blk_begin + n_my;
   u32x4* slot = nullptr;
+  u32x4 piece = {0u, 0u, 0u, 0u};
   if constexpr (kAppend) {
     __shared__ u32x4 sm_new[8][64];                     // one 1 KiB slot per wave
     slot = sm_new[threadIdx.x >> 6];
-    if (has_new) new_rows_to_lds<DT, D>(a, b, j, lane, slot);
+    if (has_new) piece = new_rows_load<DT, D>(a, b, j, lane);
   }
-  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](Tile<DT, D>& t, int tok0) {
+  // the pipelined stream, one block ahead
+  stream_blocks<DT, D, 1, true, true>(a, b, j, blk_begin, n_my, lane, bad,
+                                      [&](Tile<DT, D>& t, int tok0) {
     if constexpr (kAppend)
       if (tok0 == new_tok0) new_into_tile<DT, D>(t, slot, t_new & (kBlockTokens - 1), lane);
     // only the last block of a sequence can be partial (partitions are block aligned)
@@ -444,6 +514,9 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
       process_block<DT, D, G, true>(st, t, qf, tok0, tok_end, a.scale_log2, r);
     else
       process_block<DT, D, G, false>(st, t, qf, tok0, tok_end, a.scale_log2, r);
+  }, [&]() {
+    if constexpr (kAppend)
+      if (has_new) slot[lane] = piece;
   });
   if constexpr (kAppend)
     if (has_new) new_into_pool<DT, D>(a, slot, b, j, t_new, lane);
@@ -599,6 +672,9 @@ __device__ __forceinline__ size_t mq_row(const DecodeArgs& a, int b, int j, int 
 // stream stores the rows of the tokens in its own blocks into their pool slots. The (at
 // most two) blocks holding new tokens may belong to different waves; each writes only its
 // own blocks, which no other wave of the launch reads.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void global_void_t;
+
 template <int DT, int D, int G>
 struct NewRowsMq {
   static constexpr int kL = Geo<DT, D>::kRow / 16;      // 16-byte pieces per row
