@@ -87,6 +87,30 @@ def test_fused_step_other_shapes(dtype, d, H, Hkv):
     assert same_bits(ta["k_pool"], tb["k_pool"]) and same_bits(ta["v_pool"], tb["v_pool"])
 
 
+@pytest.mark.parametrize("dtype,H,Hkv", [("bf16", 8, 2), ("f16", 8, 8)])
+@pytest.mark.parametrize("ptok", [16, 32, 48, 64, 80, 0])
+def test_every_segment_length(dtype, H, Hkv, ptok):
+    """Fixed partitions of 1-5 blocks give every wave segments of that many blocks (the
+    sequence's last one shorter), and ptok 0 (one partition here) whole sequences of 1-7
+    blocks: a segment shorter than the prefetch distance, exactly one steady-state trip,
+    and the separate loop over the last blocks; the appended token sits at offsets 0, 7 and
+    15 of a segment's first, middle or last block. Fused step against append + decode
+    (bitwise) and against the oracle."""
+    lengths = tuple(16 * k + off for k in range(7) for off in (0, 7, 15))
+    spec = wlm.Spec(f"seglen-{dtype}-{Hkv}-{ptok}", dtype, len(lengths), H, Hkv, 128, "gqa",
+                    lengths=lengths)
+    wl = wlm.make_workload(spec, seed=ptok + Hkv)
+    a, ta = fused(wl, ptok)
+    b, tb = separate(wl, ptok)
+    assert same_bits(ta["k_pool"], tb["k_pool"]) and same_bits(ta["v_pool"], tb["v_pool"])
+    assert same_bits(a, b)
+    kp, vp = orc.kv_append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.block_tables,
+                           wl.positions, 16)
+    ref = orc.paged_decode_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                     wl.scale, wl.dtype)
+    assert_close(a.double().cpu().numpy(), ref, wl.dtype, f"segments of {ptok // 16} blocks")
+
+
 def test_bad_entries_skip_the_append_and_give_nan():
     wl = wlm.make_workload(3, small=True)
     t = wlm.to_torch(wl, DEV)
