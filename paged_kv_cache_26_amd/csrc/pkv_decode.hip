@@ -56,6 +56,21 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float as_f(unsigned u) { return __builtin_bit_cast(float, u); }
 
+// Maximum over the four 16-lane rows of each column c (lanes c, c + 16, c + 32, c + 48),
+// in every lane: the butterfly over lane bits 4 and 5 with gfx950's VALU row swaps
+// (v_permlane16_swap / v_permlane32_swap), which need neither LDS nor a wait on it, where
+// a lane shuffle is a ds_bpermute and an LDS round trip in each block's dependency chain.
+// permlane16_swap(x, x) returns rows (0, 0, 2, 2) and (1, 1, 3, 3) of x;
+// permlane32_swap(x, x) rows (0, 1, 0, 1) and (2, 3, 2, 3).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(as_f(s16[0]), as_f(s16[1]));
+  const unsigned v = __builtin_bit_cast(unsigned, y);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(as_f(s32[0]), as_f(s32[1]));
+}
+
 // Lane h of this lane's 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int H>
 __device__ __forceinline__ float row_bcast(float x) {
@@ -207,8 +222,7 @@ __device__ __forceinline__ void process_block(WaveState<DT, D, G>& st, const Til
   }
 
   float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  bm = max_over_rows(bm);
   const float m_new = fmaxf(st.m, bm);       // finite: every block has a valid token
   const float alpha = exp2_fast(st.m - m_new);
   float p[4];
@@ -576,8 +590,7 @@ __device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<
     for (int i = 0; i < 4; ++i) s[i] = acc[i] * scale_log2;
   }
   float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  bm = max_over_rows(bm);
   const float m_new = fmaxf(st.m, bm);
   // a column can see none of a block's tokens (its causal limit lies before the block)
   const float m_use = m_new == -INFINITY ? 0.f : m_new;
@@ -973,8 +986,7 @@ __device__ __forceinline__ void process_block_q(QState<DT, D>& st, const QTile<D
     if (tail) s[i] = tok0 + i < tok_end ? s[i] : -INFINITY;   // unused slots: NaN scales
   }
   float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-  bm = fmaxf(bm, __shfl_xor(bm, 16));
-  bm = fmaxf(bm, __shfl_xor(bm, 32));
+  bm = max_over_rows(bm);
   const float m_new = fmaxf(st.m, bm);            // finite: every block has a valid token
   const float alpha = exp2_fast(st.m - m_new);
   st.m = m_new;
