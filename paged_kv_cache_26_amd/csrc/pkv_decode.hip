@@ -33,7 +33,8 @@
 //     (chunk c) of token 4r + jj for jj = 0..3, and gets each head's probability for that
 //     token from lane (r, h) with a DPP row broadcast.
 // K and V are prefetched into registers one block ahead (stream_tiles_pipelined for the
-// single-query kernels, stream_tiles for the others). V rows are read with the
+// single-query kernels, stream_tiles for the multi-query and quantized ones). V rows are
+// read with the
 // non-temporal hint (each byte is used once); K keeps the default policy because two
 // consecutive loads of a wave share each 128-byte line.
 
@@ -339,9 +340,10 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
 // last iterations make it wait for every outstanding load before each fetch; there the
 // wave keeps one block in flight, fetched a whole block ahead. With kDepth = 1 this loop
 // keeps one block in flight too, but without the drains and with the last blocks in a
-// loop of their own; the single-query kernels run faster with it (the multi-query and
-// quantized ones do not, and keep stream_tiles). `begin()` runs once, right after the
-// first table entry's load is issued.
+// loop of their own; the single-query kernels (one block ahead) and the shared-prefix pass
+// (kPrefixDepth ahead) run faster with it, the multi-query and quantized kernels do not and
+// keep stream_tiles. `begin()` runs once, right after the first table entry's load is
+// issued.
 template <typename TileT, int kDepth, typename L, typename F, typename S>
 __device__ __forceinline__ void stream_tiles_pipelined(const DecodeArgs& a, int b, int blk_begin,
                                                        int n_my, int& bad, L&& load,
@@ -1662,7 +1664,7 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeArgs a) {
   int bad = 0;
   // The four waves read the same blocks, so each keeps more of them in flight than a
   // decode wave does.
-  stream_blocks<DT, D, kPrefixDepth<DT, D>, false>(a, leader, j, blk_begin, blk_end - blk_begin,
+  stream_blocks<DT, D, kPrefixDepth<DT, D>, false, true>(a, leader, j, blk_begin, blk_end - blk_begin,
                                                    lane, bad,
                                             [&](const Tile<DT, D>& tl, int tok0) {
     if (tok0 + kBlockTokens > tok_end)
