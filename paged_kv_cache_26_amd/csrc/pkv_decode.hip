@@ -34,9 +34,8 @@
 //     token from lane (r, h) with a DPP row broadcast.
 // K and V are prefetched into registers one block ahead (stream_tiles_pipelined for the
 // single-query kernels, stream_tiles for the multi-query and quantized ones). V rows are
-// read with the
-// non-temporal hint (each byte is used once); K keeps the default policy because two
-// consecutive loads of a wave share each 128-byte line.
+// read with the non-temporal hint (each byte is used once); K keeps the default policy
+// because two consecutive loads of a wave share each 128-byte line.
 
 #include "pkv_internal.h"
 
@@ -1590,9 +1589,13 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
 // with the first member's over their partition and leave one flag per (member, partition)
 // for the merge.
 // Blocks in flight per prefix-pass wave: K and V of one block take 4 * kNK + 4 * kVW
-// registers per lane; about 200 registers go to prefetch.
+// registers per lane; 64 registers go to prefetch (two blocks ahead for 16-bit d 128). On
+// the pipelined stream two blocks ahead measured fastest for the shared-prefix workload:
+// 84.4 us, against 85.4 / 85.6 / 86.7 us at 3 / 4 / 5 and 90.2 us at 8.
 template <int DT, int D>
-constexpr int kPrefixDepth = 200 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) - 1;
+constexpr int kPrefixDepth =
+    64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) > 1
+        ? 64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) : 1;
 
 template <int DT, int D, int G>
 __global__ __launch_bounds__(256) void prefix_kernel(DecodeArgs a) {
