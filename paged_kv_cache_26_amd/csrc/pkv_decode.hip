@@ -1083,7 +1083,10 @@ __device__ __forceinline__ void attend_q(QState<DT, D>& st, int& bad, const Deco
   const uint32_t v_lane = head_off + (4 * r) * tok_stride + c * QGeo<D>::kEPL;
   const char* kc = static_cast<const char*>(a.k_pool);
   const char* vc = static_cast<const char*>(a.v_pool);
-  stream_tiles<QTile<D>, 2>(
+  // Prefetch distance by format, as measured on the GQA shape: FP8 one block ahead (1.2%
+  // faster than two), INT8 two (one is 2% slower).
+  constexpr int kDepthQ = FMT == kKvFp8 ? 1 : 2;
+  stream_tiles<QTile<D>, kDepthQ>(
       a, b, blk_begin, n_my, lane, bad,
       [&](QTile<D>& t, int pb) {
         const char* kb = kc + (size_t)pb * blk_stride;
