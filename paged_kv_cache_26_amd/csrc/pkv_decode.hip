@@ -1492,8 +1492,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 
 
 // merge_kernel for many rows with few records each: one wave per output row, four rows
-// per workgroup. The wave walks the row's records in order, first for the maximum m, then
-// for l and O (lane: D / 64 consecutive elements): two rounds of loads and no barrier,
+// per workgroup. The wave reads the row's records (lane: D / 64 consecutive elements of O)
+// eight at a time in one round of loads and combines them by the rescale rule; no barrier,
 // and a quarter of the workgroups. Used when the launch has at least kMergeRowsWave rows
 // (a batch of many sequences, or q_len > 1, cuts each sequence into few segments); a few
 // long sequences, each cut into many segments, keep merge_kernel's four waves per row.
@@ -1511,7 +1511,7 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
   if (!usable(a, b, n_ctx)) return;            // decode wrote NaN
 
   size_t base, stride, pbase = 0;
-  int n_rec, n_pre = 0;
+  int n_rec, n_pre = 0, nan_row = 0;
   if (a.split) {
     const int B = a.num_seqs;
     const int G = a.n_heads / a.n_kv_heads;
@@ -1534,18 +1534,11 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
     stride = (size_t)NW * C;
     if (grp >= 0) {
       const int sb = a.group_blocks[grp];                   // <= max_blocks_per_seq here
-      int nan_row = 0;
       if (sb > a.max_shared_blocks) {
         nan_row = 1;
       } else {
         n_pre = (sb * kBlockTokens + kPrefixPartition - 1) / kPrefixPartition;
         pbase = ((size_t)b * a.n_heads + h) * a.prefix_parts;
-        for (int p = lane; p < n_pre; p += 64) nan_row |= a.ws_flags[(size_t)b * a.prefix_parts + p];
-      }
-      // the group broke its promise (see prefix_kernel): NaN row
-      if (__any(nan_row)) {
-        for (int x = lane; x < D; x += 64) store_elem<DT>(a.out, (size_t)row * D + x, __builtin_nanf(""));
-        return;
       }
     }
   } else {
@@ -1555,25 +1548,62 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
     stride = 1;
   }
 
-  float M = -INFINITY;
-#pragma unroll 4
-  for (int k = 0; k < n_rec; ++k) M = fmaxf(M, a.ws_m[base + k * stride]);
-  for (int k = 0; k < n_pre; ++k) M = fmaxf(M, a.ws_pm[pbase + k]);
-  float L = 0.f, acc[EL] = {};
-#pragma unroll 4
-  for (int k = 0; k < n_rec; ++k) {
-    const size_t r = base + k * stride;
-    const float f = exp2_fast(a.ws_m[r] - M);
-    L = fmaf(a.ws_l[r], f, L);
+  // Records k < n_rec are the segments' (base + k * stride), the next n_pre the prefix
+  // partitions' (pbase + k - n_rec). They are read kChunk at a time with every load of a
+  // chunk issued before any is used, the prefix flags of a grouped sequence in the first
+  // round too; a later chunk rescales the sums so far by 2^(M_old - M_new). Up to kChunk
+  // records this is exactly the two-pass sum (maximum first, then the weighted sums).
+  constexpr int kChunk = 8;
+  const int n_all = n_rec + n_pre;
+  float M = -INFINITY, L = 0.f, acc[EL] = {};
+  for (int k0 = 0; k0 < n_all; k0 += kChunk) {
+    float m[kChunk], l[kChunk], o[kChunk][EL];
 #pragma unroll
-    for (int e = 0; e < EL; ++e) acc[e] = fmaf(f, a.ws_o[r * D + EL * lane + e], acc[e]);
+    for (int x = 0; x < kChunk; ++x) {
+      const int k = k0 + x;
+      m[x] = -INFINITY;
+      l[x] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EL; ++e) o[x][e] = 0.f;
+      if (k < n_rec) {
+        const size_t r = base + k * stride;
+        m[x] = a.ws_m[r];
+        l[x] = a.ws_l[r];
+#pragma unroll
+        for (int e = 0; e < EL; ++e) o[x][e] = a.ws_o[r * D + EL * lane + e];
+      } else if (k < n_all) {
+        const size_t r = pbase + (k - n_rec);
+        m[x] = a.ws_pm[r];
+        l[x] = a.ws_pl[r];
+#pragma unroll
+        for (int e = 0; e < EL; ++e) o[x][e] = a.ws_po[r * D + EL * lane + e];
+      }
+    }
+    if (k0 == 0)
+      for (int p = lane; p < n_pre; p += 64) nan_row |= a.ws_flags[(size_t)b * a.prefix_parts + p];
+    if (__any(nan_row)) break;
+    float mc = M;
+#pragma unroll
+    for (int x = 0; x < kChunk; ++x)
+      if (k0 + x < n_all) mc = fmaxf(mc, m[x]);
+    const float sc = exp2_fast(M - mc);     // first chunk: M = -inf, sc = 0, sums still 0
+    L *= sc;
+#pragma unroll
+    for (int e = 0; e < EL; ++e) acc[e] *= sc;
+#pragma unroll
+    for (int x = 0; x < kChunk; ++x) {
+      if (k0 + x >= n_all) break;
+      const float f = exp2_fast(m[x] - mc);
+      L = fmaf(l[x], f, L);
+#pragma unroll
+      for (int e = 0; e < EL; ++e) acc[e] = fmaf(f, o[x][e], acc[e]);
+    }
+    M = mc;
   }
-  for (int k = 0; k < n_pre; ++k) {
-    const size_t r = pbase + k;
-    const float f = exp2_fast(a.ws_pm[r] - M);
-    L = fmaf(a.ws_pl[r], f, L);
-#pragma unroll
-    for (int e = 0; e < EL; ++e) acc[e] = fmaf(f, a.ws_po[r * D + EL * lane + e], acc[e]);
+  // the group broke its promise (see prefix_kernel): NaN row
+  if (__any(nan_row)) {
+    for (int x = lane; x < D; x += 64) store_elem<DT>(a.out, (size_t)row * D + x, __builtin_nanf(""));
+    return;
   }
   const float inv = 1.0f / L;
 #pragma unroll
