@@ -39,23 +39,31 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 # HBM bytes per decode launch (decode + merge kernels) from rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE runs, each scaled by what the counter reads for a 1 GiB device copy, keyed by
 # (workload id, partition_tokens, fused step). Each entry records the sha256 prefix of the
-# decode kernel source it was measured on; it is reported only while that source is
-# unchanged.
+# decode kernel sources it was measured on (pkv_decode.hip, then pkv_internal.h with the
+# launch constants); it is reported only while those sources are unchanged.
 MEASURED_TRAFFIC = {
-    (2, 0, True): {"bytes": 1194560470, "decode_source_sha256": "9625e5063381d47b"},
-    (2, 0, False): {"bytes": 1193454658, "decode_source_sha256": "9625e5063381d47b"},
+    (2, 0, True): {"bytes": 1194399039, "decode_source_sha256": "ca9de50a58389b05"},
+    (2, 0, False): {"bytes": 1193295680, "decode_source_sha256": "ca9de50a58389b05"},
 }
-DECODE_SOURCE = os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", "pkv_decode.hip")
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", name)
+                  for name in ("pkv_decode.hip", "pkv_internal.h")]
+
+
+def decode_source_sha() -> str:
+    """sha256 prefix of the decode kernel sources, read in DECODE_SOURCES order."""
+    import hashlib
+    h = hashlib.sha256()
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(cfg: int, partition: int, fused: bool):
-    import hashlib
     entry = MEASURED_TRAFFIC.get((cfg, partition, fused))
     if entry is None:
         return None
-    with open(DECODE_SOURCE, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()[:16]
-    return entry["bytes"] if sha == entry["decode_source_sha256"] else None
+    return entry["bytes"] if decode_source_sha() == entry["decode_source_sha256"] else None
 
 
 def parse():

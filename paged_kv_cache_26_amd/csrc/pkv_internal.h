@@ -13,7 +13,7 @@ constexpr int kFallbackPartition = 512;   // fixed partition size when the split
 constexpr int kSplitMaxSeqs = 4096;       // split mode keeps the per-sequence prefix in LDS
 constexpr int kSplitMaxWorkgroups = 1024; // upper bound of the split-mode grid
 constexpr int kSplitMinBlocks = 8;        // fewest blocks a split-mode workgroup is given
-constexpr int kMergeRowsWave = 2048;      // from this many output rows on, a wave per row
+constexpr int kMergeRowsWave = 1024;      // from this many output rows on, a wave per row
 constexpr int kPrefixPartition = 512;     // tokens per prefix-pass partition
 constexpr int kPrefixWaves = 4;           // prefix-pass waves per workgroup, 16 columns each
 constexpr int kPrefixColumns = 16 * kPrefixWaves;
