@@ -199,6 +199,23 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t n_heads, int32_t n_k
                                   int32_t partition_tokens);
 
 /*
+ * pkv_decode_split_workgroups - the grid of the balanced split on the current device: the
+ * number of workgroups the decode kernel selected by these arguments launches, i.e. the
+ * device's compute units times that kernel's own resident workgroups per compute unit
+ * (kernels differ in registers and LDS, hence in occupancy), capped at 1024. The figure is
+ * queried from the runtime once per kernel and device, then reused. fused_append != 0
+ * selects the kernels of pkv_paged_decode_step / pkv_paged_multi_query_step; kv_format 0
+ * the dtype pools, PKV_KV_INT8 / PKV_KV_FP8 (q_len 1, no fused append, dtype 16-bit) the
+ * quantized kernels. The shared-prefix decode's split pass uses the kernel of q_len 1,
+ * kv_format 0, no fused append. Host call (device attributes only, nothing is launched).
+ * Returns the workgroup count (> 0) or a negative status: PKV_ERR_DTYPE, PKV_ERR_HEAD_DIM,
+ * PKV_ERR_SHAPE, PKV_ERR_GROUP, PKV_ERR_QUERIES; PKV_ERR_LAUNCH if the runtime query fails.
+ */
+int32_t pkv_decode_split_workgroups(int32_t n_heads, int32_t n_kv_heads, int32_t d_head,
+                                    int32_t q_len, int32_t dtype, int32_t kv_format,
+                                    int32_t fused_append);
+
+/*
  * pkv_paged_multi_query_attention - q_len new query tokens per sequence attend to the
  * paged context under a causal mask (speculative verification of q_len drafted tokens,
  * or a short chunk of new tokens).

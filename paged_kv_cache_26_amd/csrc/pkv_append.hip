@@ -1,10 +1,12 @@
-// KV append (scatter of the new token into its slot), its quantizing variant, and the
-// test-only gather.
+// KV append (scatter of the new token into its slot), its quantizing variant, the
+// copy-on-write block copy, and the test-only gather.
 //
 // Slot rule, chenxutan §2.3 (write_kv / read_kv): token t of a sequence lives in the
 // physical block table[t / 16] at slot t % 16. One token's K (or V) for all KV heads is
 // one contiguous row of n_kv_heads * d_head elements in the [num_blocks, 16, n_kv_heads,
 // d_head] pool, so both kernels move whole rows with 16-byte vector accesses.
+
+#include <hip/hip_runtime.h>
 
 #include "pkv_internal.h"
 
@@ -69,6 +71,20 @@ __device__ __forceinline__ unsigned e4m3_encode(float y) {
     code = ((m + 0x7FFFFu + ((m >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
   }
   return code | ((bits >> 24) & 0x80u);
+}
+
+// grid (n_pairs, 2): y selects the K or V pool; 16 bytes per thread per step. A pair with
+// a block id outside the pool is skipped.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* k_pool, char* v_pool,
+                                                          const int32_t* pairs, int32_t num_blocks,
+                                                          int64_t block_bytes) {
+  const int32_t src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
+  if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
+  char* pool = blockIdx.y == 0 ? k_pool : v_pool;
+  const u32x4* s = reinterpret_cast<const u32x4*>(pool + src * block_bytes);
+  u32x4* d = reinterpret_cast<u32x4*>(pool + dst * block_bytes);
+  const int64_t n = block_bytes / 16;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
 }
 
 template <int DT>
@@ -182,6 +198,13 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
   const int chunks = a.row_bytes >> 4;
   const int threads = chunks < 256 ? ((chunks + 63) & ~63) : 256;
   hipLaunchKernelGGL(append_kernel, dim3(a.num_seqs, 2 * a.n_tokens), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(char* k_pool, char* v_pool, const int32_t* pairs, int32_t n_pairs,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n_pairs, 2), dim3(256), 0, stream, k_pool, v_pool,
+                     pairs, num_blocks, block_bytes);
   return hipGetLastError();
 }
 

@@ -1,5 +1,7 @@
-// Host block manager (allocation, sharing, copy-on-write) and the GPU block copy.
-// The behaviour and its sources are documented in include/pkv_block_manager.h.
+// Host block manager (allocation, sharing, copy-on-write) and the batch grouping by shared
+// leading blocks; host C++ only (the GPU block copy is in pkv_append.hip, its entry point
+// in pkv_capi.cpp). The behaviour and its sources are documented in
+// include/pkv_block_manager.h.
 
 #include "../../include/pkv_block_manager.h"
 
@@ -244,44 +246,3 @@ int32_t pkv_find_shared_prefixes(const int32_t* tables, int32_t num_seqs, int32_
 }
 
 }  // extern "C"
-
-namespace {
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// grid (n_pairs, 2): y selects the K or V pool; 16 bytes per thread per step.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(char* k_pool, char* v_pool,
-                                                          const int32_t* pairs, int32_t num_blocks,
-                                                          int64_t block_bytes) {
-  const int32_t src = pairs[2 * blockIdx.x], dst = pairs[2 * blockIdx.x + 1];
-  if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
-  char* pool = blockIdx.y == 0 ? k_pool : v_pool;
-  const u32x4* s = reinterpret_cast<const u32x4*>(pool + src * block_bytes);
-  u32x4* d = reinterpret_cast<u32x4*>(pool + dst * block_bytes);
-  const int64_t n = block_bytes / 16;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) d[i] = s[i];
-}
-
-}  // namespace
-
-extern "C" int32_t pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs,
-                                   int32_t n_pairs, int32_t num_blocks, int32_t block_size,
-                                   int32_t n_kv_heads, int32_t d_head, int32_t dtype,
-                                   hipStream_t stream) {
-  if (!k_pool || !v_pool || (n_pairs > 0 && !pairs)) return PKV_ERR_NULL;
-  const int32_t eb = dtype == PKV_F32 ? 4 : (dtype == PKV_F16 || dtype == PKV_BF16) ? 2 : 0;
-  if (eb == 0) return PKV_ERR_DTYPE;
-  if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
-  if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
-  if (n_pairs < 0 || n_pairs > 65535 || num_blocks <= 0 || n_kv_heads <= 0 ||
-      n_kv_heads > pkv::kMaxKvHeads)
-    return PKV_ERR_SHAPE;
-  if ((reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15u)
-    return PKV_ERR_ALIGN;
-  if (n_pairs == 0) return PKV_OK;
-  const int64_t block_bytes = (int64_t)block_size * n_kv_heads * d_head * eb;
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n_pairs, 2), dim3(256), 0, stream,
-                     static_cast<char*>(k_pool), static_cast<char*>(v_pool), pairs, num_blocks,
-                     block_bytes);
-  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
-}

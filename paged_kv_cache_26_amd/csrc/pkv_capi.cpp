@@ -1,5 +1,6 @@
-// C ABI of libpkv: host-side argument checks, workspace sizing and kernel dispatch.
-// The operations and their sources are documented in include/pkv.h.
+// C ABI of libpkv: host-side argument checks, workspace sizing and kernel dispatch (host
+// C++; the kernels are behind the launchers of pkv_internal.h). The operations and their
+// sources are documented in include/pkv.h and include/pkv_block_manager.h.
 
 #include "../../include/pkv.h"
 #include "../../include/pkv_block_manager.h"
@@ -399,6 +400,34 @@ int32_t pkv_paged_decode_attention(void* out, const void* q, const void* k_pool,
                      workspace_bytes, stream);
 }
 
+int32_t pkv_decode_split_workgroups(int32_t n_heads, int32_t n_kv_heads, int32_t d_head,
+                                    int32_t q_len, int32_t dtype, int32_t kv_format,
+                                    int32_t fused_append) {
+  if (elem_bytes(dtype) == 0) return PKV_ERR_DTYPE;
+  if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
+  if (n_kv_heads <= 0 || n_kv_heads > pkv::kMaxKvHeads) return PKV_ERR_SHAPE;
+  if (!valid_group(n_heads, n_kv_heads)) return PKV_ERR_GROUP;
+  if (!valid_q_len(q_len, n_heads, n_kv_heads)) return PKV_ERR_QUERIES;
+  if (kv_format != 0 && ((kv_format != PKV_KV_INT8 && kv_format != PKV_KV_FP8) ||
+                         dtype == PKV_F32 || q_len != 1 || fused_append))
+    return PKV_ERR_DTYPE;
+  int32_t grid = 0;
+  pkv::DecodeArgs a{};
+  a.n_heads = n_heads;
+  a.n_kv_heads = n_kv_heads;
+  a.q_len = q_len;
+  a.split = 1;
+  a.grid_out = &grid;
+  static const char kNonNull = 0;               // selects the fused-append kernels
+  a.k_new = fused_append ? &kNonNull : nullptr;
+  a.v_new = a.k_new;
+  const hipError_t e =
+      kv_format ? pkv::launch_decode_quantized(a, dtype, kv_format, d_head, n_heads / n_kv_heads,
+                                               nullptr)
+                : pkv::launch_decode(a, dtype, d_head, n_heads / n_kv_heads, nullptr);
+  return e == hipSuccess && grid > 0 ? grid : PKV_ERR_LAUNCH;
+}
+
 size_t pkv_multi_query_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t n_heads,
                                        int32_t n_kv_heads, int32_t d_head,
                                        int32_t max_context_len, int32_t partition_tokens) {
@@ -517,6 +546,26 @@ int32_t pkv_paged_decode_attention_shared_prefix(
   a.ws_po = reinterpret_cast<float*>(take(plan.shared_records * d_head * sizeof(float)));
   a.ws_flags = reinterpret_cast<int32_t*>(take(plan.flag_ints * sizeof(int32_t)));
   const hipError_t e = pkv::launch_shared_prefix(a, dtype, d_head, g, stream);
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+int32_t pkv_copy_blocks(void* k_pool, void* v_pool, const int32_t* pairs, int32_t n_pairs,
+                        int32_t num_blocks, int32_t block_size, int32_t n_kv_heads,
+                        int32_t d_head, int32_t dtype, hipStream_t stream) {
+  if (!k_pool || !v_pool || (n_pairs > 0 && !pairs)) return PKV_ERR_NULL;
+  const int32_t eb = elem_bytes(dtype);
+  if (eb == 0) return PKV_ERR_DTYPE;
+  if (block_size != pkv::kBlockTokens) return PKV_ERR_BLOCK_SIZE;
+  if (d_head != 64 && d_head != 128) return PKV_ERR_HEAD_DIM;
+  if (n_pairs < 0 || n_pairs > 65535 || num_blocks <= 0 || n_kv_heads <= 0 ||
+      n_kv_heads > pkv::kMaxKvHeads)
+    return PKV_ERR_SHAPE;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_ALIGN;
+  if (n_pairs == 0) return PKV_OK;
+  const int64_t block_bytes = (int64_t)block_size * n_kv_heads * d_head * eb;
+  const hipError_t e = pkv::launch_copy_blocks(static_cast<char*>(k_pool),
+                                               static_cast<char*>(v_pool), pairs, n_pairs,
+                                               num_blocks, block_bytes, stream);
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

@@ -37,7 +37,15 @@
 // read with the non-temporal hint (each byte is used once); K keeps the default policy
 // because two consecutive loads of a wave share each 128-byte line.
 
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
 #include "pkv_internal.h"
+
+#ifndef PKV_DECODE_DTYPE
+#error "compile pkv_decode.hip once per dtype: -DPKV_DECODE_DTYPE=0 (f32), 1 (f16) or 2 (bf16)"
+#endif
 
 namespace pkv {
 namespace {
@@ -1730,28 +1738,44 @@ __global__ __launch_bounds__(256) void prefix_kernel(DecodeArgs a) {
   }
 }
 
-// Resident workgroups of a kernel on the current device (queried once per kernel).
-template <typename K>
-int resident_workgroups(K kernel, int threads) {
-  static int per_cu = -1;
-  if (per_cu < 0) {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
-    per_cu = n;
+// Resident workgroups of kernel K on the current device: compute units times the
+// kernel's own occupancy. K is a template argument, so every kernel instantiation keeps
+// its own figures (instantiations differ in registers and LDS, hence in occupancy); they
+// are queried once per device and kept per device. Concurrent first calls store the same
+// value.
+constexpr int kMaxDevices = 64;
+
+template <auto K>
+int resident_workgroups(int threads) {
+  static std::atomic<int> cached[kMaxDevices];   // 0: not queried yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < kMaxDevices ? dev : kMaxDevices - 1;
+  int n = dev < kMaxDevices ? cached[slot].load(std::memory_order_relaxed) : 0;
+  if (n <= 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, K, threads, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 1;
+    n = per_cu * cus;
+    if (dev < kMaxDevices) cached[slot].store(n, std::memory_order_relaxed);
   }
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 1;
-  return per_cu * cus;
+  return n;
 }
 
 template <int DT, int D, int G, int NW, int MODE>
 hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
   bool need_merge;
   if (a.split) {
-    auto kernel = decode_split_kernel<DT, D, G, NW, MODE>;
-    a.split_workgroups = min(kSplitMaxWorkgroups, resident_workgroups(kernel, 64 * NW));
+    constexpr auto kernel = decode_split_kernel<DT, D, G, NW, MODE>;
+    a.split_workgroups = min(kSplitMaxWorkgroups, resident_workgroups<kernel>(64 * NW));
+    if (a.grid_out) {                             // grid query: report, launch nothing
+      *a.grid_out = a.split_workgroups;
+      return hipSuccess;
+    }
     hipLaunchKernelGGL(kernel, dim3(a.split_workgroups), dim3(64 * NW), 0, stream, a);
     need_merge = true;
   } else {
@@ -1865,30 +1889,28 @@ hipError_t launch_prefix_dim(const DecodeArgs& a, int d_head, int group, hipStre
 
 }  // namespace
 
-hipError_t launch_shared_prefix(const DecodeArgs& a, int dtype, int d_head, int group,
-                                hipStream_t stream) {
-  switch (dtype) {
-    case 0: return launch_prefix_dim<0>(a, d_head, group, stream);
-    case 1: return launch_prefix_dim<1>(a, d_head, group, stream);
-    case 2: return launch_prefix_dim<2>(a, d_head, group, stream);
-    default: return hipErrorInvalidValue;
-  }
+// The launchers of this translation unit's dtype (pkv_dispatch.cpp selects among them).
+template <>
+hipError_t launch_decode_dtype<PKV_DECODE_DTYPE>(const DecodeArgs& a, int d_head, int group,
+                                                 hipStream_t stream) {
+  return launch_dim<PKV_DECODE_DTYPE>(a, d_head, group, stream);
 }
 
-hipError_t launch_decode_quantized(const DecodeArgs& a, int dtype, int kv_format, int d_head,
-                                   int group, hipStream_t stream) {
-  if (kv_format != kKvInt8 && kv_format != kKvFp8) return hipErrorInvalidValue;
-  if (dtype == 1) return launch_quant_dtype<1>(a, kv_format, d_head, group, stream);
-  if (dtype == 2) return launch_quant_dtype<2>(a, kv_format, d_head, group, stream);
-  return hipErrorInvalidValue;
+template <>
+hipError_t launch_shared_prefix_dtype<PKV_DECODE_DTYPE>(const DecodeArgs& a, int d_head,
+                                                        int group, hipStream_t stream) {
+  return launch_prefix_dim<PKV_DECODE_DTYPE>(a, d_head, group, stream);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int dtype, int d_head, int group, hipStream_t stream) {
-  switch (dtype) {
-    case 0: return launch_dim<0>(a, d_head, group, stream);
-    case 1: return launch_dim<1>(a, d_head, group, stream);
-    case 2: return launch_dim<2>(a, d_head, group, stream);
-    default: return hipErrorInvalidValue;
+template <>
+hipError_t launch_decode_quantized_dtype<PKV_DECODE_DTYPE>(const DecodeArgs& a, int kv_format,
+                                                           int d_head, int group,
+                                                           hipStream_t stream) {
+  if constexpr (PKV_DECODE_DTYPE == 0) {
+    return hipErrorInvalidValue;               // q and out must be 16-bit over 8-bit codes
+  } else {
+    if (kv_format != kKvInt8 && kv_format != kKvFp8) return hipErrorInvalidValue;
+    return launch_quant_dtype<PKV_DECODE_DTYPE>(a, kv_format, d_head, group, stream);
   }
 }
 

@@ -1,7 +1,9 @@
-// Internal launch interface between the C ABI (pkv_capi.hip) and the kernels.
+// Internal launch interface between the C ABI (pkv_capi.cpp, host C++) and the kernels
+// (*.hip). Host-only declarations: the C ABI and the block manager include it from plain
+// C++ translation units.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -97,6 +99,9 @@ struct DecodeArgs {
   // [num_seqs][n_kv_heads][d_head]; the token is context_lens[b] - 1. nullptr: no append.
   const char* k_new;
   const char* v_new;
+  // Grid query (host side only): when set, the split-mode launcher stores the grid it would
+  // use here and launches nothing.
+  int32_t* grid_out;
 };
 
 // Quantizing append: one token per sequence, K and V rows of every KV head quantized to
@@ -118,13 +123,29 @@ struct QuantAppendArgs {
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_append_quantized(const QuantAppendArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t stream);
+// pool[dst] = pool[src] in both pools for each (src, dst) pair; block_bytes per block.
+hipError_t launch_copy_blocks(char* k_pool, char* v_pool, const int32_t* pairs, int32_t n_pairs,
+                              int32_t num_blocks, int64_t block_bytes, hipStream_t stream);
 // dtype: 0 f32, 1 f16, 2 bf16; d_head 64/128; group 1/2/4/8 (validated by the caller).
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int d_head, int group,
                          hipStream_t stream);
-// Shared-prefix decode (split mode, q_len 1): prefix pass, split pass, merge.
+// Decode over 8-bit codes (dtype 1 or 2 for q / out).
 hipError_t launch_decode_quantized(const DecodeArgs& a, int dtype, int kv_format, int d_head,
                                    int group, hipStream_t stream);
+// Shared-prefix decode (split mode, q_len 1): prefix pass, split pass, merge.
 hipError_t launch_shared_prefix(const DecodeArgs& a, int dtype, int d_head, int group,
                                 hipStream_t stream);
+
+// The decode kernels of one dtype DT. pkv_decode.hip is compiled once per dtype
+// (-DPKV_DECODE_DTYPE=DT) and defines these three for its DT; launch_decode,
+// launch_decode_quantized and launch_shared_prefix (pkv_dispatch.cpp) pick the dtype.
+template <int DT>
+hipError_t launch_decode_dtype(const DecodeArgs& a, int d_head, int group, hipStream_t stream);
+template <int DT>
+hipError_t launch_decode_quantized_dtype(const DecodeArgs& a, int kv_format, int d_head,
+                                         int group, hipStream_t stream);
+template <int DT>
+hipError_t launch_shared_prefix_dtype(const DecodeArgs& a, int d_head, int group,
+                                      hipStream_t stream);
 
 }  // namespace pkv

@@ -2,6 +2,8 @@
 // rate that the decode kernels are compared with (the second denominator of their
 // roofline, next to the published peak).
 
+#include <hip/hip_runtime.h>
+
 #include "../../include/pkv.h"
 
 #include "pkv_internal.h"

@@ -79,6 +79,7 @@ _SIGNATURES = {
                                                                           _c_i32, _c_ptr,
                                                                           _c_size, _c_ptr]),
     "pkv_stream_read": (_c_i32, [_c_ptr, _c_size, _c_ptr, _c_size, _c_i32, _c_ptr]),
+    "pkv_decode_split_workgroups": (_c_i32, [_c_i32] * 7),
     "pkv_find_shared_prefixes": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr,
                                           _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
 }
@@ -131,9 +132,46 @@ def _require(cond: bool, msg: str) -> None:
 
 
 def _check_device(*tensors: torch.Tensor) -> None:
+    """Every tensor on the GPU, contiguous, and all on the same device."""
     for t in tensors:
         _require(t.is_cuda, "tensors must be on the GPU")
         _require(t.is_contiguous(), "tensors must be contiguous")
+    _require(len({t.device for t in tensors}) <= 1, "tensors must be on the same device")
+
+
+def _opt(t):
+    """() for None, else (t,): optional tensors in an argument list."""
+    return () if t is None else (t,)
+
+
+def _check_tables(block_tables: torch.Tensor, B: int) -> None:
+    """[>= B, max_blocks_per_seq >= 1] int32: the kernels read row b for every b < B."""
+    _require(block_tables.dtype == torch.int32, "block_tables must be int32")
+    _require(block_tables.dim() == 2 and block_tables.shape[0] >= B and block_tables.shape[1] >= 1,
+             f"block_tables must be [B, max_blocks_per_seq] with at least B = {B} rows")
+
+
+def _check_per_seq(t: torch.Tensor, B: int, name: str) -> None:
+    """A 1-D int32 vector with at least B entries (context lengths, positions, groups)."""
+    _require(t.dtype == torch.int32, f"{name} must be int32")
+    _require(t.dim() == 1 and t.numel() >= B, f"{name} must be 1-D with at least B = {B} entries")
+
+
+def _check_pools(k_pool: torch.Tensor, v_pool: torch.Tensor, d: int | None = None) -> None:
+    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape,
+             "pools must be [num_blocks, 16, H_kv, d] and of one shape")
+    if d is not None:
+        _require(k_pool.shape[3] == d, "the pools' d_head must equal q's")
+
+
+def _new_workspace(need: int, device, stream):
+    """A workspace from torch's allocator, allocated on the stream the kernels use: the
+    caching allocator then reuses its bytes only for work ordered after them on that
+    stream, even when it is not the current stream."""
+    if stream is None:
+        return torch.empty(need, dtype=torch.uint8, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(need, dtype=torch.uint8, device=device)
 
 
 def pkv_status_str(status: int) -> str:
@@ -153,13 +191,15 @@ def pkv_decode_workspace_bytes(num_seqs: int, n_heads: int, n_kv_heads: int, d_h
 def pkv_kv_append(k_pool, v_pool, k_new, v_new, block_tables, positions, stream=None) -> None:
     """Write k_new/v_new [B, H_kv, d] into the pools at positions[b] (in place)."""
     lib = load_library()
-    _check_device(k_pool, v_pool, k_new, v_new, block_tables, positions)
-    _require(k_pool.dtype in _DTYPE_CODE, "unsupported dtype")
-    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pools must be [N, 16, H_kv, d]")
-    _require(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [B, H_kv, d]")
-    _require(block_tables.dtype == torch.int32 and positions.dtype == torch.int32,
-             "tables and positions must be int32")
+    _require(k_pool.dtype in _DTYPE_CODE and k_pool.dtype == v_pool.dtype == k_new.dtype ==
+             v_new.dtype, "pools and new rows must share a supported dtype")
+    _check_pools(k_pool, v_pool)
+    _require(k_new.shape == v_new.shape and k_new.dim() == 3 and k_new.shape[1:] == k_pool.shape[2:],
+             "k_new/v_new must be [B, H_kv, d] with the pools' H_kv and d")
     B = k_new.shape[0]
+    _check_tables(block_tables, B)
+    _check_per_seq(positions, B, "positions")
+    _check_device(k_pool, v_pool, k_new, v_new, block_tables, positions)
     st = lib.pkv_kv_append(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
                            _ptr(block_tables), _ptr(positions), B, block_tables.shape[1],
                            k_pool.shape[0], k_pool.shape[1], k_pool.shape[2], k_pool.shape[3],
@@ -178,19 +218,19 @@ def pkv_paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_len
     Returns ``out``.
     """
     lib = load_library()
-    _check_device(out, q, k_pool, v_pool, block_tables, context_lens)
     _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype,
              "q, out and pools must share a supported dtype")
     _require(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, H, d]")
-    _require(k_pool.dim() == 4 and k_pool.shape == v_pool.shape, "pools must be [N, 16, H_kv, d]")
-    _require(block_tables.dtype == torch.int32 and context_lens.dtype == torch.int32,
-             "tables and lengths must be int32")
     B, H, d = q.shape
+    _check_pools(k_pool, v_pool, d)
+    _check_tables(block_tables, B)
+    _check_per_seq(context_lens, B, "context_lens")
+    _check_device(out, q, k_pool, v_pool, block_tables, context_lens, *_opt(workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = pkv_decode_workspace_bytes(B, H, k_pool.shape[2], d, max_context_len, partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _new_workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pkv_paged_decode_attention(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
@@ -205,21 +245,25 @@ def pkv_paged_decode_attention(out, q, k_pool, v_pool, block_tables, context_len
 def pkv_paged_decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
                           max_context_len: int, scale: float | None = None,
                           partition_tokens: int = 0, workspace=None, stream=None):
-    """pkv_kv_append (token context_lens[b] - 1) and pkv_paged_decode_attention in one
-    launch. Returns out."""
+    """pkv_kv_append (token context_lens[b] - 1) and pkv_paged_decode_attention in one call
+    (the decode kernel with the append fused in, then the merge kernel). Returns out."""
     lib = load_library()
-    _check_device(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens)
     _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype ==
              k_new.dtype == v_new.dtype, "q, out, pools and new rows must share a dtype")
     _require(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, H, d]")
-    _require(k_new.shape == v_new.shape and k_new.shape == (q.shape[0], k_pool.shape[2], q.shape[2]),
-             "k_new/v_new must be [B, H_kv, d]")
     B, H, d = q.shape
+    _check_pools(k_pool, v_pool, d)
+    _require(k_new.shape == v_new.shape and k_new.shape == (B, k_pool.shape[2], d),
+             "k_new/v_new must be [B, H_kv, d]")
+    _check_tables(block_tables, B)
+    _check_per_seq(context_lens, B, "context_lens")
+    _check_device(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                  *_opt(workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = pkv_decode_workspace_bytes(B, H, k_pool.shape[2], d, max_context_len, partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _new_workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pkv_paged_decode_step(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
@@ -235,11 +279,15 @@ def pkv_kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, positions,
                          stream=None) -> None:
     """Write k_new/v_new [B, n_tokens, H_kv, d] at positions[b] + i (in place)."""
     lib = load_library()
-    _check_device(k_pool, v_pool, k_new, v_new, block_tables, positions)
-    _require(k_pool.dtype in _DTYPE_CODE, "unsupported dtype")
-    _require(k_new.shape == v_new.shape and k_new.dim() == 4,
-             "k_new/v_new must be [B, n_tokens, H_kv, d]")
+    _require(k_pool.dtype in _DTYPE_CODE and k_pool.dtype == v_pool.dtype == k_new.dtype ==
+             v_new.dtype, "pools and new rows must share a supported dtype")
+    _check_pools(k_pool, v_pool)
+    _require(k_new.shape == v_new.shape and k_new.dim() == 4 and k_new.shape[2:] == k_pool.shape[2:],
+             "k_new/v_new must be [B, n_tokens, H_kv, d] with the pools' H_kv and d")
     B, n = k_new.shape[0], k_new.shape[1]
+    _check_tables(block_tables, B)
+    _check_per_seq(positions, B, "positions")
+    _check_device(k_pool, v_pool, k_new, v_new, block_tables, positions)
     st = lib.pkv_kv_append_tokens(_ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
                                   _ptr(block_tables), _ptr(positions), B, n,
                                   block_tables.shape[1], k_pool.shape[0], k_pool.shape[1],
@@ -247,6 +295,20 @@ def pkv_kv_append_tokens(k_pool, v_pool, k_new, v_new, block_tables, positions,
                                   _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_kv_append_tokens")
+
+
+def pkv_decode_split_workgroups(n_heads: int, n_kv_heads: int, d_head: int, q_len: int = 1,
+                                dtype=torch.bfloat16, kv_format=0,
+                                fused_append: bool = False) -> int:
+    """Workgroups of the balanced split's decode kernel for these arguments on the current
+    device (compute units x that kernel's resident workgroups per compute unit)."""
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    fmt = 0 if kv_format in (0, None) else _kv_format(kv_format)
+    n = int(load_library().pkv_decode_split_workgroups(n_heads, n_kv_heads, d_head, q_len, code,
+                                                       fmt, int(bool(fused_append))))
+    if n <= 0:
+        raise PkvError(n, "pkv_decode_split_workgroups")
+    return n
 
 
 def pkv_multi_query_workspace_bytes(num_seqs: int, q_len: int, n_heads: int, n_kv_heads: int,
@@ -261,17 +323,20 @@ def pkv_paged_multi_query_attention(out, q, k_pool, v_pool, block_tables, contex
                                     partition_tokens: int = 0, workspace=None, stream=None):
     """q/out [B, q_len, H, d]; new query i of sequence b sees tokens < N_b - q_len + i + 1."""
     lib = load_library()
-    _check_device(out, q, k_pool, v_pool, block_tables, context_lens)
     _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype,
              "q, out and pools must share a supported dtype")
     _require(q.dim() == 4 and out.shape == q.shape, "q/out must be [B, q_len, H, d]")
     B, ql, H, d = q.shape
+    _check_pools(k_pool, v_pool, d)
+    _check_tables(block_tables, B)
+    _check_per_seq(context_lens, B, "context_lens")
+    _check_device(out, q, k_pool, v_pool, block_tables, context_lens, *_opt(workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = pkv_multi_query_workspace_bytes(B, ql, H, k_pool.shape[2], d, max_context_len,
                                            partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _new_workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pkv_paged_multi_query_attention(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
@@ -287,22 +352,27 @@ def pkv_paged_multi_query_step(out, q, k_pool, v_pool, k_new, v_new, block_table
                                max_context_len: int, scale: float | None = None,
                                partition_tokens: int = 0, workspace=None, stream=None):
     """pkv_kv_append_tokens (tokens context_lens[b] - q_len ..) and
-    pkv_paged_multi_query_attention in one launch; k_new/v_new [B, q_len, H_kv, d].
+    pkv_paged_multi_query_attention in one call (the decode kernel with the appends fused
+    in, then the merge kernel); k_new/v_new [B, q_len, H_kv, d].
     Returns out."""
     lib = load_library()
-    _check_device(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens)
     _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype ==
              k_new.dtype == v_new.dtype, "q, out, pools and new rows must share a dtype")
     _require(q.dim() == 4 and out.shape == q.shape, "q/out must be [B, q_len, H, d]")
     B, ql, H, d = q.shape
+    _check_pools(k_pool, v_pool, d)
     _require(k_new.shape == v_new.shape and k_new.shape == (B, ql, k_pool.shape[2], d),
              "k_new/v_new must be [B, q_len, H_kv, d]")
+    _check_tables(block_tables, B)
+    _check_per_seq(context_lens, B, "context_lens")
+    _check_device(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens,
+                  *_opt(workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = pkv_multi_query_workspace_bytes(B, ql, H, k_pool.shape[2], d, max_context_len,
                                            partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _new_workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pkv_paged_multi_query_step(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
@@ -330,17 +400,23 @@ def pkv_paged_decode_attention_shared_prefix(out, q, k_pool, v_pool, block_table
     seq_group [B] int32 (group id or -1), group_blocks [n_groups] int32 (shared blocks).
     """
     lib = load_library()
-    _check_device(out, q, k_pool, v_pool, block_tables, context_lens, seq_group, group_blocks)
     _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype,
              "q, out and pools must share a supported dtype")
-    _require(seq_group.dtype == torch.int32 and group_blocks.dtype == torch.int32,
-             "seq_group and group_blocks must be int32")
+    _require(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, H, d]")
     B, H, d = q.shape
+    _check_pools(k_pool, v_pool, d)
+    _check_tables(block_tables, B)
+    _check_per_seq(context_lens, B, "context_lens")
+    _check_per_seq(seq_group, B, "seq_group")
+    _require(group_blocks.dtype == torch.int32 and group_blocks.dim() == 1 and
+             group_blocks.numel() >= 1, "group_blocks must be a non-empty 1-D int32 vector")
+    _check_device(out, q, k_pool, v_pool, block_tables, context_lens, seq_group, group_blocks,
+                  *_opt(workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = pkv_shared_prefix_workspace_bytes(B, H, k_pool.shape[2], d, max_shared_blocks)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = _new_workspace(max(need, 1), q.device, stream)
     ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.pkv_paged_decode_attention_shared_prefix(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_tables), _ptr(context_lens),
@@ -364,7 +440,6 @@ def pkv_kv_append_quantized(k_codes, v_codes, k_scales, v_scales, k_new, v_new, 
     """Quantize k_new/v_new [B, H_kv, d] into the uint8 code pools [N, 16, H_kv, d] and the
     (s, z) pools [N, H_kv, 16, 2] at positions[b] (in place)."""
     lib = load_library()
-    _check_device(k_codes, v_codes, k_scales, v_scales, k_new, v_new, block_tables, positions)
     _require(k_codes.dtype == torch.uint8 and v_codes.dtype == torch.uint8, "codes must be uint8")
     _require(k_scales.dtype == torch.float32 and v_scales.dtype == torch.float32,
              "scales must be float32")
@@ -373,7 +448,11 @@ def pkv_kv_append_quantized(k_codes, v_codes, k_scales, v_scales, k_new, v_new, 
     N, bs, Hkv, d = k_codes.shape
     _require(k_scales.shape == (N, Hkv, bs, 2) and v_scales.shape == k_scales.shape,
              "scales must be [N, H_kv, 16, 2]")
-    _require(k_new.shape == v_new.shape and k_new.dim() == 3, "k_new/v_new must be [B, H_kv, d]")
+    _require(k_new.shape == v_new.shape and k_new.dim() == 3 and k_new.shape[1:] == (Hkv, d),
+             "k_new/v_new must be [B, H_kv, d] with the code pools' H_kv and d")
+    _check_tables(block_tables, k_new.shape[0])
+    _check_per_seq(positions, k_new.shape[0], "positions")
+    _check_device(k_codes, v_codes, k_scales, v_scales, k_new, v_new, block_tables, positions)
     st = lib.pkv_kv_append_quantized(
         _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales), _ptr(k_new), _ptr(v_new),
         _ptr(block_tables), _ptr(positions), k_new.shape[0], block_tables.shape[1], N, bs, Hkv,
@@ -389,18 +468,25 @@ def pkv_paged_decode_attention_quantized(out, q, k_codes, v_codes, k_scales, v_s
                                          stream=None):
     """pkv_paged_decode_attention over a quantized cache (q/out f16 or bf16). Returns out."""
     lib = load_library()
-    _check_device(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens)
     _require(q.dtype in (torch.float16, torch.bfloat16) and out.dtype == q.dtype,
              "q and out must be f16 or bf16")
     _require(k_codes.dtype == torch.uint8 and v_codes.dtype == torch.uint8, "codes must be uint8")
     _require(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, H, d]")
     B, H, d = q.shape
+    _check_pools(k_codes, v_codes, d)
     N, bs, Hkv, _ = k_codes.shape
+    _require(k_scales.dtype == torch.float32 and v_scales.dtype == torch.float32 and
+             k_scales.shape == (N, Hkv, bs, 2) and v_scales.shape == k_scales.shape,
+             "scales must be float32 [N, H_kv, 16, 2]")
+    _check_tables(block_tables, B)
+    _check_per_seq(context_lens, B, "context_lens")
+    _check_device(out, q, k_codes, v_codes, k_scales, v_scales, block_tables, context_lens,
+                  *_opt(workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     need = pkv_decode_workspace_bytes(B, H, Hkv, d, max_context_len, partition_tokens)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _new_workspace(need, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.pkv_paged_decode_attention_quantized(
         _ptr(out), _ptr(q), _ptr(k_codes), _ptr(v_codes), _ptr(k_scales), _ptr(v_scales),
@@ -416,8 +502,8 @@ def pkv_stream_read(buf, sink, workgroups: int = 0, nbytes: int | None = None,
                     stream=None) -> None:
     """Read nbytes (default: all) of the GPU tensor buf once (streaming-read ceiling)."""
     lib = load_library()
-    _check_device(buf, sink)
     _require(sink.dtype == torch.int32 or sink.dtype == torch.uint32, "sink must be 32-bit")
+    _check_device(buf, sink)
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     st = lib.pkv_stream_read(_ptr(buf), n, _ptr(sink), sink.numel(), int(workgroups),
                              _stream(stream))
@@ -429,8 +515,17 @@ def pkv_gather_kv(k_out, v_out, k_pool, v_pool, block_tables, context_lens,
                   max_context_len: int, stream=None) -> None:
     """Copy each sequence's used K/V rows into k_out/v_out [B, max_context_len, H_kv, d]."""
     lib = load_library()
-    _check_device(k_out, v_out, k_pool, v_pool, block_tables, context_lens)
+    _check_pools(k_pool, v_pool)
+    _check_tables(block_tables, 1)
     B = block_tables.shape[0]
+    _check_per_seq(context_lens, B, "context_lens")
+    _require(k_out.dtype == v_out.dtype == k_pool.dtype == v_pool.dtype,
+             "outputs and pools must share a dtype")
+    _require(k_out.shape == v_out.shape and k_out.dim() == 4 and
+             k_out.shape[0] >= B and k_out.shape[1] >= int(max_context_len) and
+             k_out.shape[2:] == k_pool.shape[2:],
+             "k_out/v_out must be [B, max_context_len, H_kv, d]")
+    _check_device(k_out, v_out, k_pool, v_pool, block_tables, context_lens)
     st = lib.pkv_gather_kv(_ptr(k_out), _ptr(v_out), _ptr(k_pool), _ptr(v_pool),
                            _ptr(block_tables), _ptr(context_lens), B, block_tables.shape[1],
                            k_pool.shape[0], int(max_context_len), k_pool.shape[1],
@@ -443,9 +538,11 @@ def pkv_gather_kv(k_out, v_out, k_pool, v_pool, block_tables, context_lens,
 def pkv_copy_blocks(k_pool, v_pool, pairs, stream=None) -> None:
     """pool[dst] = pool[src] in both pools for every row (src, dst) of pairs [n, 2] int32."""
     lib = load_library()
-    _check_device(k_pool, v_pool, pairs)
     _require(pairs.dtype == torch.int32 and pairs.dim() == 2 and pairs.shape[1] == 2,
              "pairs must be int32 [n, 2]")
+    _check_pools(k_pool, v_pool)
+    _require(k_pool.dtype == v_pool.dtype, "pools must share a dtype")
+    _check_device(k_pool, v_pool, pairs)
     st = lib.pkv_copy_blocks(_ptr(k_pool), _ptr(v_pool), _ptr(pairs), pairs.shape[0],
                              k_pool.shape[0], k_pool.shape[1], k_pool.shape[2], k_pool.shape[3],
                              _DTYPE_CODE[k_pool.dtype], _stream(stream))

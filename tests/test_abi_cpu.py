@@ -229,3 +229,101 @@ def test_multi_query_step_rejects_bad_arguments_on_host(lib):
         args[idx] = val
         assert f(*args) == code, (idx, val)
     assert f(*good) == -9                     # the balanced split needs its workspace
+
+
+# ---------------------------------------------------------------------------------------
+# The binding's own checks: shapes the kernels index without a bound (table rows, lengths,
+# positions for every b < B; the pools' head size) and the device of every tensor are
+# checked before any call into the library, so these run without a GPU.
+# ---------------------------------------------------------------------------------------
+
+def _cpu_decode_args(B=4, H=8, Hkv=2, d=64, nb=32, mbps=8, dtype=None):
+    import torch
+    dtype = dtype or torch.float16
+    return dict(out=torch.zeros(B, H, d, dtype=dtype), q=torch.zeros(B, H, d, dtype=dtype),
+                k_pool=torch.zeros(nb, 16, Hkv, d, dtype=dtype),
+                v_pool=torch.zeros(nb, 16, Hkv, d, dtype=dtype),
+                block_tables=torch.zeros(B, mbps, dtype=torch.int32),
+                context_lens=torch.ones(B, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("bad,match", [
+    (dict(block_tables=(3, 8)), "block_tables"),        # fewer rows than sequences
+    (dict(block_tables=(32,)), "block_tables"),          # not 2-D
+    (dict(context_lens=(3,)), "context_lens"),           # fewer lengths than sequences
+    (dict(context_lens=(4, 1)), "context_lens"),         # not 1-D
+    (dict(pool_d=128), "d_head"),                        # pools' head size differs from q's
+    (dict(), "on the GPU"),                              # shapes fine, tensors on the CPU
+])
+def test_decode_binding_checks_shapes_before_any_launch(lib, bad, match):
+    import torch
+    a = _cpu_decode_args()
+    if "block_tables" in bad:
+        a["block_tables"] = torch.zeros(bad["block_tables"], dtype=torch.int32)
+    if "context_lens" in bad:
+        a["context_lens"] = torch.ones(bad["context_lens"], dtype=torch.int32)
+    if "pool_d" in bad:
+        a["k_pool"] = torch.zeros(32, 16, 2, bad["pool_d"], dtype=torch.float16)
+        a["v_pool"] = torch.zeros_like(a["k_pool"])
+    with pytest.raises(ValueError, match=match):
+        pkv.pkv_paged_decode_attention(a["out"], a["q"], a["k_pool"], a["v_pool"],
+                                       a["block_tables"], a["context_lens"], 16)
+    k_new = torch.zeros(4, 2, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match=match):
+        pkv.pkv_paged_decode_step(a["out"], a["q"], a["k_pool"], a["v_pool"], k_new, k_new,
+                                  a["block_tables"], a["context_lens"], 16)
+    q4 = a["q"].reshape(4, 1, 8, 64)
+    with pytest.raises(ValueError, match=match):
+        pkv.pkv_paged_multi_query_attention(q4.clone(), q4, a["k_pool"], a["v_pool"],
+                                            a["block_tables"], a["context_lens"], 16)
+
+
+def test_append_binding_checks_shapes_before_any_launch(lib):
+    import torch
+    a = _cpu_decode_args()
+    k_new = torch.zeros(4, 2, 64, dtype=torch.float16)
+    pos = torch.zeros(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="positions"):
+        pkv.pkv_kv_append(a["k_pool"], a["v_pool"], k_new, k_new, a["block_tables"], pos[:3])
+    with pytest.raises(ValueError, match="block_tables"):
+        pkv.pkv_kv_append(a["k_pool"], a["v_pool"], k_new, k_new, a["block_tables"][:2], pos)
+    wide = torch.zeros(4, 3, 64, dtype=torch.float16)      # 3 KV heads against the pools' 2
+    with pytest.raises(ValueError, match="H_kv"):
+        pkv.pkv_kv_append(a["k_pool"], a["v_pool"], wide, wide, a["block_tables"], pos)
+    with pytest.raises(ValueError, match="dtype"):
+        pkv.pkv_kv_append(a["k_pool"], a["v_pool"], k_new.float(), k_new.float(),
+                          a["block_tables"], pos)
+    with pytest.raises(ValueError, match="on the GPU"):
+        pkv.pkv_kv_append(a["k_pool"], a["v_pool"], k_new, k_new, a["block_tables"], pos)
+    k4 = k_new.reshape(4, 1, 2, 64)
+    with pytest.raises(ValueError, match="positions"):
+        pkv.pkv_kv_append_tokens(a["k_pool"], a["v_pool"], k4, k4, a["block_tables"], pos[:1])
+
+
+def test_shared_prefix_and_quantized_bindings_check_shapes(lib):
+    import torch
+    a = _cpu_decode_args(dtype=torch.bfloat16)
+    sg = torch.zeros(4, dtype=torch.int32)
+    gb = torch.ones(1, dtype=torch.int32)
+    with pytest.raises(ValueError, match="seq_group"):
+        pkv.pkv_paged_decode_attention_shared_prefix(
+            a["out"], a["q"], a["k_pool"], a["v_pool"], a["block_tables"], a["context_lens"],
+            sg[:2], gb, 4, 1, 16)
+    with pytest.raises(ValueError, match="context_lens"):
+        pkv.pkv_paged_decode_attention_shared_prefix(
+            a["out"], a["q"], a["k_pool"], a["v_pool"], a["block_tables"], a["context_lens"][:1],
+            sg, gb, 4, 1, 16)
+    codes = torch.zeros(32, 16, 2, 64, dtype=torch.uint8)
+    scales = torch.zeros(32, 2, 16, 2, dtype=torch.float32)
+    with pytest.raises(ValueError, match="block_tables"):
+        pkv.pkv_paged_decode_attention_quantized(a["out"], a["q"], codes, codes, scales, scales,
+                                                 a["block_tables"][:1], a["context_lens"], 16,
+                                                 "int8")
+    with pytest.raises(ValueError, match="scales"):
+        pkv.pkv_paged_decode_attention_quantized(a["out"], a["q"], codes, codes, scales[:, :1],
+                                                 scales, a["block_tables"], a["context_lens"],
+                                                 16, "int8")
+    k_new = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="positions"):
+        pkv.pkv_kv_append_quantized(codes, codes, scales, scales, k_new, k_new,
+                                    a["block_tables"], torch.zeros(2, dtype=torch.int32), "fp8")
