@@ -16,3 +16,15 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def root_dir():
     return ROOT
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With PKV_PARITY_RECORD=<file>, write every parity comparison's achieved errors."""
+    path = os.environ.get("PKV_PARITY_RECORD")
+    if not path:
+        return
+    from tests import parity
+    if not parity.RECORDS:
+        return
+    with open(path, "w") as f:
+        f.write(parity.records_table())

@@ -140,10 +140,31 @@ def test_bad_entries_skip_the_append_and_give_nan():
 
 def test_many_rows_use_the_wave_per_row_merge():
     """20 sequences x 4 new tokens x 32 heads = 2560 output rows: the merge runs one wave
-    per row (from 2048 rows on); the result must still match the oracle."""
+    per row (from 1024 rows on); the result must still match the oracle."""
     wl = mq_workload(4, B=20, lo=600, hi=2500, seed=21)
     out, t = check_against_separate(wl, 0)
     kp, vp = oracle_pools(wl)
     ref = orc.paged_multi_query_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
                                           wl.scale, "bf16")
     assert_close(out.double().cpu().numpy(), ref, "bf16", "many rows")
+
+
+@pytest.mark.slow
+def test_full_size_gqa_verify4():
+    """The benchmark's multi-query shape: the GQA workload (64 sequences of 4096-8192
+    tokens, 32 / 8 heads, d 128, bf16) with 4 new tokens per sequence, fused step bitwise
+    equal to the two calls, pools bit-exact, every output against the oracle."""
+    import dataclasses
+    print("multi-query full size, q_len 4", flush=True)
+    spec = dataclasses.replace(wlm.SPECS[3], name="gqa-bf16-verify4", q_len=4)
+    wl = wlm.make_workload(spec, seed=3)
+    out, t = check_against_separate(wl, 0)
+    kp, vp = oracle_pools(wl)
+    for name, ref_pool in (("k_pool", kp), ("v_pool", vp)):
+        ref_dev = torch.from_numpy(ref_pool.view(np.int16)).to(DEV)
+        assert torch.equal(t[name].view(torch.int16), ref_dev), name
+        del ref_dev
+    ref = orc.paged_multi_query_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                          wl.scale, "bf16")
+    e = assert_close(out.double().cpu().numpy(), ref, "bf16", "verify4 full size")
+    print(f"  errors {e}", flush=True)

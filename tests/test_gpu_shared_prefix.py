@@ -111,20 +111,16 @@ def test_equals_plain_decode_within_bars():
     assert_close(got, out.double().cpu().numpy(), "bf16", "vs plain decode")
 
 
-def test_full_size_shared_prefix_workload_sampled():
+@pytest.mark.slow
+def test_full_size_shared_prefix_workload():
     """128 sequences in 8 groups of 16 over a 2048-token prefix, the launch the benchmark
-    times; the oracle checks sampled (sequence, head) rows."""
+    times; every output against the oracle."""
     _log("shared prefix: full-size workload")
     wl = wlm.make_workload(5)
     got, _ = gpu_shared(wl)
-    rng = np.random.default_rng(5)
-    seqs = sorted(rng.choice(wl.batch, size=6, replace=False).tolist())
-    pairs = [(b, h) for b in seqs for h in sorted(rng.choice(32, size=4, replace=False).tolist())]
-    ref = oracle_out(wl, pairs=pairs)
-    b = np.array([p[0] for p in pairs])
-    h = np.array([p[1] for p in pairs])
-    assert_close(got[b, h], ref[b, h], "bf16", "full size sampled")
     assert np.isfinite(got).all()
+    e = assert_close(got, oracle_out(wl), "bf16", "full size")
+    _log(f"  errors {e}")
 
 
 def test_member_with_a_different_table_gets_nan():

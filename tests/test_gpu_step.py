@@ -66,13 +66,29 @@ def test_fused_step_matches_append_then_decode(cfg, ptok):
     assert_close(a.double().cpu().numpy(), ref, wl.dtype, f"fused cfg {cfg}")
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
 def test_fused_step_full_size(cfg):
+    """The benchmark's launch at full size: bitwise equal to append + decode, pools
+    bit-exact against the oracle's append, every output against the oracle."""
+    print(f"fused step full size cfg {cfg}", flush=True)
     wl = wlm.make_workload(cfg)
     a, ta = fused(wl)
     b, tb = separate(wl)
     assert same_bits(a, b)
     assert same_bits(ta["k_pool"], tb["k_pool"]) and same_bits(ta["v_pool"], tb["v_pool"])
+    del tb
+    kp, vp = orc.kv_append(wl.k_pool, wl.v_pool, wl.k_new, wl.v_new, wl.block_tables,
+                           wl.positions, 16)
+    view = np.int16 if wl.dtype != "f32" else np.int32
+    for name, ref_pool in (("k_pool", kp), ("v_pool", vp)):
+        ref_dev = torch.from_numpy(ref_pool.view(view)).to(DEV)
+        assert torch.equal(ta[name].view(ref_dev.dtype), ref_dev), name
+        del ref_dev
+    ref = orc.paged_decode_attention(wl.q, kp, vp, wl.block_tables, wl.context_lens, 16,
+                                     wl.scale, wl.dtype)
+    e = assert_close(a.double().cpu().numpy(), ref, wl.dtype, f"fused full cfg {cfg}")
+    print(f"  errors {e}", flush=True)
 
 
 @pytest.mark.parametrize("dtype,d,H,Hkv", [("f32", 64, 8, 2), ("f16", 128, 8, 1),
