@@ -42,8 +42,10 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 # decode kernel sources it was measured on (pkv_decode.hip, then pkv_internal.h with the
 # launch constants); it is reported only while those sources are unchanged.
 MEASURED_TRAFFIC = {
-    (2, 0, True): {"bytes": 1194399039, "decode_source_sha256": "ca9de50a58389b05"},
-    (2, 0, False): {"bytes": 1193295680, "decode_source_sha256": "ca9de50a58389b05"},
+    (3, 0, True): {"bytes": 1587428921, "decode_source_sha256": "bc7517ee4d4a1772"},
+    (3, 0, False): {"bytes": 1586840921, "decode_source_sha256": "bc7517ee4d4a1772"},
+    (4, 0, True): {"bytes": 1352597256, "decode_source_sha256": "bc7517ee4d4a1772"},
+    (4, 0, False): {"bytes": 1352548256, "decode_source_sha256": "bc7517ee4d4a1772"},
 }
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", name)
                   for name in ("pkv_decode.hip", "pkv_internal.h")]
