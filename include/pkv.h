@@ -71,7 +71,8 @@ enum pkv_status {
   PKV_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch */
   PKV_ERR_ALIGN = -11,      /* a device pointer is not 16-byte aligned */
   PKV_ERR_ALIAS = -12,      /* out overlaps q, k_pool or v_pool */
-  PKV_ERR_QUERIES = -17     /* q_len < 1 or q_len * (n_heads / n_kv_heads) > 16 */
+  PKV_ERR_QUERIES = -17,    /* q_len < 1 or q_len * (n_heads / n_kv_heads) > 16 */
+  PKV_ERR_SCRATCH = -18     /* the sizes need more than the static scratch's 32 MiB */
 };
 
 /*
@@ -180,6 +181,31 @@ int32_t pkv_paged_decode_step(void* out, const void* q, void* k_pool, void* v_po
                               int32_t n_kv_heads, int32_t d_head, float scale,
                               int32_t partition_tokens, int32_t dtype, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * pkv_paged_decode_step_noalloc - pkv_paged_decode_step without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation). Its partial-result records live in a static
+ * device array of the library (32 MiB, one copy per device, held from the first call on a
+ * device until the process ends); the call itself allocates nothing.
+ *
+ * Arguments, outputs and errors as pkv_paged_decode_step, plus PKV_ERR_SCRATCH when the
+ * sizes need more workspace than 32 MiB (pkv_decode_workspace_bytes(num_seqs, n_heads,
+ * n_kv_heads, d_head, max_context_len, partition_tokens) > 32 MiB; for example 128
+ * sequences of 32 / 8 heads, d_head 128, need 19 MB), found on the host before anything is
+ * enqueued. The scratch needs no clearing: every record is written before it is read
+ * within a call, and its contents between calls do not matter. All calls on one device
+ * share its scratch, so calls that overlap in time on one device (different streams, or
+ * host threads without ordering) race and give wrong results; serialise them (one stream).
+ */
+int32_t pkv_paged_decode_step_noalloc(void* out, const void* q, void* k_pool, void* v_pool,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int32_t num_blocks, int32_t max_context_len,
+                                      int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+                                      int32_t d_head, float scale, int32_t partition_tokens,
+                                      int32_t dtype, hipStream_t stream);
 
 /*
  * pkv_decode_workspace_bytes - scratch bytes pkv_paged_decode_attention needs for these

@@ -30,6 +30,7 @@ UNITS = [
     ("pkv_block_manager", "pkv_block_manager.cpp", []),
     ("pkv_append", "pkv_append.hip", []),
     ("pkv_measure", "pkv_measure.hip", []),
+    ("pkv_scratch", "pkv_scratch.hip", []),
     ("pkv_decode_f32", "pkv_decode.hip", ["-DPKV_DECODE_DTYPE=0"]),
     ("pkv_decode_f16", "pkv_decode.hip", ["-DPKV_DECODE_DTYPE=1"]),
     ("pkv_decode_bf16", "pkv_decode.hip", ["-DPKV_DECODE_DTYPE=2"]),

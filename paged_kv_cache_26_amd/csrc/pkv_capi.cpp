@@ -9,6 +9,7 @@
 #include <cmath>
 
 #include "pkv_internal.h"
+#include "pkv_scratch.h"
 
 namespace {
 
@@ -125,7 +126,8 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
                     int32_t dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
                     int32_t kv_format = 0, const float* k_scales = nullptr,
                     const float* v_scales = nullptr, const void* k_new = nullptr,
-                    const void* v_new = nullptr, bool fused_append = false) {
+                    const void* v_new = nullptr, bool fused_append = false,
+                    bool static_scratch = false) {
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_NULL;
   if (fused_append && (!k_new || !v_new)) return PKV_ERR_NULL;
   if (kv_format != 0 && (!k_scales || !v_scales)) return PKV_ERR_NULL;
@@ -167,6 +169,12 @@ int32_t decode_impl(void* out, const void* q, const void* k_pool, const void* v_
   const Plan plan = make_plan(num_seqs, q_len, n_heads, n_kv_heads, d_head, max_context_len,
                               partition_tokens);
   if (!plan.split && plan.parts > 65535) return PKV_ERR_PARTITION;   // grid y limit
+  if (static_scratch && plan.bytes > 0) {     // the library's static scratch, every check done
+    if (plan.bytes > pkv::kScratchBytes) return PKV_ERR_SCRATCH;
+    workspace = pkv::scratch_region();
+    workspace_bytes = pkv::kScratchBytes;
+    if (!workspace) return PKV_ERR_LAUNCH;
+  }
   if (plan.bytes > 0 && (!workspace || workspace_bytes < plan.bytes || !aligned16(workspace)))
     return PKV_ERR_WORKSPACE;
 
@@ -233,6 +241,7 @@ const char* pkv_status_str(int32_t status) {
     case PKV_ERR_SEQUENCE_EXISTS: return "sequence id already in use";
     case PKV_ERR_BAD_BLOCK: return "block id outside the pool";
     case PKV_ERR_QUERIES: return "q_len must be >= 1 with q_len * (n_heads / n_kv_heads) <= 16";
+    case PKV_ERR_SCRATCH: return "the sizes need more workspace than the library's 32 MiB static scratch";
     default: return "unknown status";
   }
 }
@@ -342,6 +351,20 @@ int32_t pkv_paged_decode_step(void* out, const void* q, void* k_pool, void* v_po
                      max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
                      n_kv_heads, d_head, scale, partition_tokens, dtype, workspace,
                      workspace_bytes, stream, 0, nullptr, nullptr, k_new, v_new, true);
+}
+
+int32_t pkv_paged_decode_step_noalloc(void* out, const void* q, void* k_pool, void* v_pool,
+                                      const void* k_new, const void* v_new,
+                                      const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t num_seqs, int32_t max_blocks_per_seq,
+                                      int32_t num_blocks, int32_t max_context_len,
+                                      int32_t block_size, int32_t n_heads, int32_t n_kv_heads,
+                                      int32_t d_head, float scale, int32_t partition_tokens,
+                                      int32_t dtype, hipStream_t stream) {
+  return decode_impl(out, q, k_pool, v_pool, block_tables, context_lens, num_seqs, 1,
+                     max_blocks_per_seq, num_blocks, max_context_len, block_size, n_heads,
+                     n_kv_heads, d_head, scale, partition_tokens, dtype, nullptr, 0, stream, 0,
+                     nullptr, nullptr, k_new, v_new, true, /*static_scratch=*/true);
 }
 
 int32_t pkv_paged_decode_attention_quantized(

@@ -80,6 +80,9 @@ _SIGNATURES = {
                                                                           _c_size, _c_ptr]),
     "pkv_stream_read": (_c_i32, [_c_ptr, _c_size, _c_ptr, _c_size, _c_i32, _c_ptr]),
     "pkv_decode_split_workgroups": (_c_i32, [_c_i32] * 7),
+    "pkv_paged_decode_step_noalloc": (_c_i32, [_c_ptr] * 8 + [_c_i32] * 8 + [ctypes.c_float,
+                                                                             _c_i32, _c_i32,
+                                                                             _c_ptr]),
     "pkv_find_shared_prefixes": (_c_i32, [_c_ptr, _c_i32, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr,
                                           _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
 }
@@ -272,6 +275,36 @@ def pkv_paged_decode_step(out, q, k_pool, v_pool, k_new, v_new, block_tables, co
         int(partition_tokens), _DTYPE_CODE[q.dtype], _ptr(workspace), ws_bytes, _stream(stream))
     if st != 0:
         raise PkvError(st, "pkv_paged_decode_step")
+    return out
+
+
+def pkv_paged_decode_step_noalloc(out, q, k_pool, v_pool, k_new, v_new, block_tables,
+                                  context_lens, max_context_len: int,
+                                  scale: float | None = None, partition_tokens: int = 0,
+                                  stream=None):
+    """pkv_paged_decode_step with the library's static device scratch as its workspace: the
+    call allocates nothing. Calls that overlap on one device share that scratch and race.
+    Returns out."""
+    lib = load_library()
+    _require(q.dtype in _DTYPE_CODE and out.dtype == q.dtype == k_pool.dtype == v_pool.dtype ==
+             k_new.dtype == v_new.dtype, "q, out, pools and new rows must share a dtype")
+    _require(q.dim() == 3 and out.shape == q.shape, "q/out must be [B, H, d]")
+    B, H, d = q.shape
+    _check_pools(k_pool, v_pool, d)
+    _require(k_new.shape == v_new.shape and k_new.shape == (B, k_pool.shape[2], d),
+             "k_new/v_new must be [B, H_kv, d]")
+    _check_tables(block_tables, B)
+    _check_per_seq(context_lens, B, "context_lens")
+    _check_device(out, q, k_pool, v_pool, k_new, v_new, block_tables, context_lens)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib.pkv_paged_decode_step_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_new), _ptr(v_new),
+        _ptr(block_tables), _ptr(context_lens), B, block_tables.shape[1], k_pool.shape[0],
+        int(max_context_len), k_pool.shape[1], H, k_pool.shape[2], d, float(scale),
+        int(partition_tokens), _DTYPE_CODE[q.dtype], _stream(stream))
+    if st != 0:
+        raise PkvError(st, "pkv_paged_decode_step_noalloc")
     return out
 
 

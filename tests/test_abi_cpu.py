@@ -79,7 +79,7 @@ def test_workspace_bytes(lib):
 
 def test_status_strings(lib):
     assert pkv.pkv_status_str(0) == "ok"
-    for code in range(-17, 0):
+    for code in range(-18, 0):
         s = pkv.pkv_status_str(code)
         assert s and s != "unknown status"
     assert pkv.pkv_status_str(5) == "unknown status"
@@ -327,3 +327,20 @@ def test_shared_prefix_and_quantized_bindings_check_shapes(lib):
     with pytest.raises(ValueError, match="positions"):
         pkv.pkv_kv_append_quantized(codes, codes, scales, scales, k_new, k_new,
                                     a["block_tables"], torch.zeros(2, dtype=torch.int32), "fp8")
+
+
+def test_noalloc_step_rejects_sizes_beyond_its_scratch_on_host(lib):
+    """4096 sequences of 64 / 8 heads need far more than the 32 MiB static scratch: the
+    call returns PKV_ERR_SCRATCH before touching the device (the pointers are fake)."""
+    f = lib.pkv_paged_decode_step_noalloc
+    # out, q, k_pool, v_pool, k_new, v_new, tables, lens, B, maxb, nb, maxctx, bs, H, Hkv, d,
+    # scale, partition, dtype, stream
+    g = 1 << 32                               # fake buffers 4 GiB apart: no overlap
+    args = [1 * g, 2 * g, 3 * g, 4 * g, 5 * g, 6 * g, 7 * g, 8 * g, 4096, 64, 64, 700, 16, 64, 8,
+            128, 0.1, 0, 2, None]
+    assert pkv.pkv_decode_workspace_bytes(4096, 64, 8, 128, 700, 0) > 32 << 20
+    assert f(*args) == -18
+    assert "32 MiB" in pkv.pkv_status_str(-18)
+    bad = list(args)
+    bad[8], bad[15] = 4, 96                   # a small batch with an unsupported head size
+    assert f(*bad) == -4
