@@ -11,6 +11,12 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workloads")
+    # tests/test_host_sanitizers.py runs the host-code tests against a sanitized build of
+    # the host C++ with launcher stubs; the binding then loads that library instead
+    lib = os.environ.get("PKV_TEST_LIBRARY")
+    if lib:
+        from paged_kv_cache_26_amd import pkv
+        pkv.load_library(lib)
 
 
 @pytest.fixture(scope="session")
