@@ -328,17 +328,31 @@ def stream_ceiling(nbytes: int, dev, reps: int = 10) -> dict:
                     "of the step's KV bytes", "gbps": round(best, 1), "workgroups": best_wg}
 
 
+def _flush_buffer(dev):
+    """A 1 GiB buffer, written once. Reading it (flush_caches) evicts the 256 MB last-level
+    cache (MALL) and the L2s and leaves them holding clean lines: a flush by writing would
+    leave ~0.3 GB of dirty lines that the next kernel has to write back first."""
+    import torch
+    buf = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    flush_caches(buf)
+    return buf
+
+
+def flush_caches(buf):
+    buf.sum()                                # a reduction kernel reads every byte
+
+
 def cold_steps(step, args, by, dev, stream) -> dict:
-    """The same step with the 256 MB last-level cache (MALL) flushed before each one by
-    writing a 1 GiB scratch buffer outside the timed region (shared blocks then come
+    """The same step with the 256 MB last-level cache (MALL) and the L2s flushed before
+    each one by reading a 1 GiB buffer outside the timed region (shared blocks then come
     from HBM every step)."""
     import torch
 
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush = _flush_buffer(dev)
     K = args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     for i in range(K):
-        flush.fill_(i & 0xFF)
+        flush_caches(flush)
         ev[i][0].record(stream)
         step(ev[i][1])
         ev[i][2].record(stream)
@@ -352,7 +366,7 @@ def cold_steps(step, args, by, dev, stream) -> dict:
             "decode_us_mean": round(dec_s * 1e6, 2),
             "decode_kv_gbps_logical": round(by["kv"] / dec_s / 1e9, 1),
             "decode_unique_gbps": round(by["kv_unique"] / dec_s / 1e9, 1),
-            "flush": "1 GiB written before each step, outside the timed region"}
+            "flush": "a 1 GiB buffer read before each step, outside the timed region"}
 
 
 def _cpu_model() -> str:
@@ -529,6 +543,26 @@ def _time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps * 1e-3           # seconds per launch sequence
 
 
+def _time_cold(fn, steps, dev):
+    """Mean duration (s) of fn with the 256 MB last-level cache (MALL) and the L2s flushed
+    before each call by reading a 1 GiB buffer; HIP events bracket each call alone."""
+    import torch
+    flush = _flush_buffer(dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        flush_caches(flush)
+        ev[i][0].record(stream)
+        fn()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    del flush
+    torch.cuda.empty_cache()
+    return t
+
+
 def run_multi_query(args) -> dict:
     """q_len new tokens per sequence verified in one pass vs q_len single-token steps.
 
@@ -672,6 +706,8 @@ def run_shared_prefix(args) -> dict:
     s_step = _time_launches(step, args.steps, args.warmup)
     s_shared = _time_launches(shared, args.steps, args.warmup)
     s_plain = _time_launches(plain, args.steps, args.warmup)
+    cold_shared = _time_cold(shared, args.steps, dev)
+    cold_plain = _time_cold(plain, args.steps, dev)
     by = algorithmic_bytes(wl)
     q_out = 2 * wl.q.nbytes
     tables = int(sum(-(-int(n) // 16) for n in wl.context_lens)) * 4
@@ -697,6 +733,12 @@ def run_shared_prefix(args) -> dict:
         "plain_decode_attention_us": round(s_plain * 1e6, 2),
         "speedup_vs_plain_decode": round(s_plain / s_shared, 2),
         "unique_kv_gbps": round(by["kv_unique"] / s_shared / 1e9, 1),
+        "cold": {"attention_us_mean": round(cold_shared * 1e6, 2),
+                 "plain_decode_attention_us_mean": round(cold_plain * 1e6, 2),
+                 "unique_kv_gbps": round(by["kv_unique"] / cold_shared / 1e9, 1),
+                 "frac_of_hbm_peak_unique": round(alg / cold_shared / 1e9 / HBM_PEAK_GBPS, 4),
+                 "flush": "a 1 GiB buffer read before each call, outside the timed call, so "
+                          "the shared prefix comes from HBM"},
         "host_grouping_us": round(group_us, 1),
         "roofline": {"bound": "hbm", "kernel": "shared-prefix decode launch (prefix pass, split "
                      "pass, merge)", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
