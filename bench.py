@@ -36,16 +36,25 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 
-# HBM bytes per decode launch (decode + merge kernels) from rocprofv3 --pmc FETCH_SIZE and
-# WRITE_SIZE runs, each scaled by what the counter reads for a 1 GiB device copy, keyed by
-# (workload id, partition_tokens, fused step). Each entry records the sha256 prefix of the
-# decode kernel sources it was measured on (pkv_decode.hip, then pkv_internal.h with the
-# launch constants); it is reported only while those sources are unchanged.
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs, each scaled by
+# what the counter reads for a 1 GiB device copy. Decode step lines are keyed by (workload
+# id, partition_tokens, fused step) and cover the decode + merge kernels; the component
+# lines by ("multi-query", q_len) (decode + merge of the attention call), ("shared-prefix",)
+# (prefix pass + split pass + merge) and ("quantized", format) (decode + merge). Each entry
+# records the sha256 prefix of the decode kernel sources it was measured on (pkv_decode.hip,
+# then pkv_internal.h with the launch constants); it is reported only while those sources
+# are unchanged.
 MEASURED_TRAFFIC = {
     (3, 0, True): {"bytes": 1587428921, "decode_source_sha256": "bc7517ee4d4a1772"},
     (3, 0, False): {"bytes": 1586840921, "decode_source_sha256": "bc7517ee4d4a1772"},
     (4, 0, True): {"bytes": 1352597256, "decode_source_sha256": "bc7517ee4d4a1772"},
     (4, 0, False): {"bytes": 1352548256, "decode_source_sha256": "bc7517ee4d4a1772"},
+    (2, 0, True): {"bytes": 1194417000, "decode_source_sha256": "bc7517ee4d4a1772"},
+    (2, 0, False): {"bytes": 1193308000, "decode_source_sha256": "bc7517ee4d4a1772"},
+    ("multi-query", 4): {"bytes": 1628014000, "decode_source_sha256": "bc7517ee4d4a1772"},
+    ("shared-prefix",): {"bytes": 392350700, "decode_source_sha256": "bc7517ee4d4a1772"},
+    ("quantized", "int8"): {"bytes": 849612100, "decode_source_sha256": "bc7517ee4d4a1772"},
+    ("quantized", "fp8"): {"bytes": 849537000, "decode_source_sha256": "bc7517ee4d4a1772"},
 }
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", name)
                   for name in ("pkv_decode.hip", "pkv_internal.h")]
@@ -61,8 +70,8 @@ def decode_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg: int, partition: int, fused: bool):
-    entry = MEASURED_TRAFFIC.get((cfg, partition, fused))
+def measured_traffic(*key):
+    entry = MEASURED_TRAFFIC.get(tuple(key))
     if entry is None:
         return None
     return entry["bytes"] if decode_source_sha() == entry["decode_source_sha256"] else None
@@ -278,15 +287,7 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
     if cfg == 5:
         res["cold"] = cold_steps(step, args, by, dev, stream)
     if args.copy_calibration:
-        n = args.copy_calibration << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_calibration_bytes"] = {"read": n, "write": n}
-        del src, dst
+        res["copy_calibration_bytes"] = copy_calibration(args.copy_calibration)
     if cfg == 5:
         res["timing"]["decode_unique_gbps"] = round(by["kv_unique"] / dec_avg_s / 1e9, 2)
     if want_cpu:
@@ -295,6 +296,22 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
     del t, out, ws
     torch.cuda.empty_cache()
     return res
+
+
+def copy_calibration(mib: int) -> dict:
+    """Three device copies of exactly mib MiB: dispatches of known traffic for scaling the
+    hardware byte counters (FETCH_SIZE, WRITE_SIZE)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"read": n, "write": n}
 
 
 def stream_ceiling(nbytes: int, dev, reps: int = 10) -> dict:
@@ -650,9 +667,11 @@ def run_multi_query(args) -> dict:
         "attention_us": round(s_attn * 1e6, 2),
         "sequential_single_query_us": round(s_seq * 1e6, 2),
         "speedup_vs_sequential": round(s_seq / s_step, 2),
-        "roofline": {"bound": "hbm", "kernel": "multi-query decode launch", "achieved": round(gbps, 1),
+        "roofline": {"bound": "hbm", "kernel": "pkv_paged_multi_query_attention call: decode "
+                     "kernel, then the merge kernel", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": alg},
+                     "traffic": measured_traffic("multi-query", ql),
+                     "algorithmic_bytes_per_launch": alg},
     }
 
 
@@ -740,9 +759,10 @@ def run_shared_prefix(args) -> dict:
                  "flush": "a 1 GiB buffer read before each call, outside the timed call, so "
                           "the shared prefix comes from HBM"},
         "host_grouping_us": round(group_us, 1),
-        "roofline": {"bound": "hbm", "kernel": "shared-prefix decode launch (prefix pass, split "
-                     "pass, merge)", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+        "roofline": {"bound": "hbm", "kernel": "pkv_paged_decode_attention_shared_prefix call: "
+                     "prefix pass, split pass, merge", "achieved": round(gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("shared-prefix"),
                      "algorithmic_bytes_per_launch": alg},
     }
 
@@ -822,9 +842,11 @@ def run_quantized(args) -> dict:
         "bf16_cache_attention_us": round(s_bf16 * 1e6, 2),
         "speedup_vs_bf16_cache": round(s_bf16 / s_attn, 2),
         "context_tokens_per_s": round(tokens / s_attn, 1),
-        "roofline": {"bound": "hbm", "kernel": f"{fmt}-cache decode launch (decode + merge)",
+        "roofline": {"bound": "hbm", "kernel": f"pkv_paged_decode_attention_quantized call "
+                     f"({fmt} cache): decode kernel, then the merge kernel",
                      "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("quantized", fmt),
                      "algorithmic_bytes_per_launch": alg},
     }
 
@@ -840,6 +862,8 @@ def main():
     if args.component == "block-manager":
         print(json.dumps(run_block_manager(args)), flush=True)
         return
+    if args.component != "decode" and args.copy_calibration:
+        copy_calibration(args.copy_calibration)
     if args.component == "multi-query":
         print(json.dumps(run_multi_query(args)), flush=True)
         return
