@@ -175,12 +175,13 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
     def run(fn, per_step):
         """K steps after W warm-up ones; per_step brackets each step (and, for the
         two-launch step, its decode launch) with events, otherwise only the K-step
-        region is bracketed."""
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
+        region is bracketed. The events are made before the warm-up, so the GPU does not
+        sit idle between the warm-up and the timed region (after idle time it needs tens
+        of steps to return to its sustained rate)."""
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(args.warmup):
+            fn()
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         e0.record(stream)
@@ -201,9 +202,14 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
         la = (np.array([e[1].elapsed_time(e[2]) for e in ev]) if fn is separate_step else st)
         return total, wall_s, st, la
 
-    # The streaming-read ceiling of the line, measured first: its ~50 full-bandwidth sweeps
-    # also bring the GPU to its sustained clocks before the step's own warm-up.
-    ceiling = stream_ceiling(algorithmic_bytes(wl)["kv"], dev)
+    # The split grid of the step's decode kernel (a host query, which also loads the kernel's
+    # code object now rather than during the warm-up).
+    split_grid = pkv.pkv_decode_split_workgroups(wl.spec.n_heads, wl.spec.n_kv_heads,
+                                                 wl.spec.d_head, 1, t["q"].dtype, 0, fused)
+    # The streaming-read ceiling of the line, measured first and right before the warm-up:
+    # its ~50 full-bandwidth sweeps keep the GPU busy up to the step's own warm-up (its
+    # buffers are released after the timed region, so nothing idles the GPU in between).
+    ceiling = stream_ceiling(algorithmic_bytes(wl)["kv"], dev, release=False)
     # The timed region. The fused step is one call (decode kernel + merge kernel), so the
     # region's time per step is that call's duration (the gap between the kernels included)
     # and no per-step events (each costs a few microseconds of GPU time) are recorded in
@@ -216,6 +222,7 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
     dec_avg_s = ms_per_step * 1e-3 if fused else float(dec_ms.mean()) * 1e-3
     launch_bytes = by["decode"] + (by["append"] if fused else 0)
     achieved = launch_bytes / dec_avg_s / 1e9
+    torch.cuda.empty_cache()                 # the ceiling's buffers
     # After the timed region: per-step event spread of the fused step, and the other
     # form of the step timed like the timed region.
     if fused:
@@ -246,8 +253,8 @@ def run_config(args, cfg: int, want_cpu: bool) -> dict:
             "d_head": spec.d_head, "block_size": 16,
             "context_tokens": int(wl.context_lens.sum()),
             "max_context_len": wl.max_context_len,
-            "kv_split": ("balanced split over the GPU" if args.partition == 0
-                         else f"fixed {args.partition}-token partitions"),
+            "kv_split": (f"balanced split over the GPU ({split_grid} workgroups)"
+                         if args.partition == 0 else f"fixed {args.partition}-token partitions"),
             "step": ("one call, pkv_paged_decode_step: the decode kernel with the append fused "
                      "in, then the partition merge kernel"
                      if fused else "two calls: pkv_kv_append, then pkv_paged_decode_attention "
@@ -314,9 +321,11 @@ def copy_calibration(mib: int) -> dict:
     return {"read": n, "write": n}
 
 
-def stream_ceiling(nbytes: int, dev, reps: int = 10) -> dict:
+def stream_ceiling(nbytes: int, dev, reps: int = 10, release: bool = True) -> dict:
     """The achievable read rate: pkv_stream_read over a fresh buffer of nbytes (rounded up
-    to 16), best over a few grid sizes, HIP events on the current stream."""
+    to 16), best over a few grid sizes, HIP events on the current stream. release=False
+    leaves the buffers in torch's cache (no device free, no idle gap) for the caller to
+    release later."""
     import torch
 
     from paged_kv_cache_26_amd import pkv
@@ -340,7 +349,8 @@ def stream_ceiling(nbytes: int, dev, reps: int = 10) -> dict:
         if gbps > best:
             best, best_wg = gbps, wg
     del buf, sink
-    torch.cuda.empty_cache()
+    if release:
+        torch.cuda.empty_cache()
     return {"kind": "streaming read (pkv_stream_read, 16-byte non-temporal loads) of a buffer "
                     "of the step's KV bytes", "gbps": round(best, 1), "workgroups": best_wg}
 
