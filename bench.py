@@ -40,7 +40,7 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 # what the counter reads for a 1 GiB device copy. Decode step lines are keyed by (workload
 # id, partition_tokens, fused step) and cover the decode + merge kernels; the component
 # lines by ("multi-query", q_len) (decode + merge of the attention call), ("shared-prefix",)
-# (prefix pass + split pass + merge) and ("quantized", format) (decode + merge). Each entry
+# (split kernel with the prefix tasks + merge) and ("quantized", format) (decode + merge). Each entry
 # records the sha256 prefix of the decode kernel sources it was measured on (pkv_decode.hip,
 # then pkv_internal.h with the launch constants); it is reported only while those sources
 # are unchanged.
@@ -770,7 +770,7 @@ def run_shared_prefix(args) -> dict:
                           "the shared prefix comes from HBM"},
         "host_grouping_us": round(group_us, 1),
         "roofline": {"bound": "hbm", "kernel": "pkv_paged_decode_attention_shared_prefix call: "
-                     "prefix pass, split pass, merge", "achieved": round(gbps, 1),
+                     "split kernel with the prefix tasks, then the merge", "achieved": round(gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic("shared-prefix"),
                      "algorithmic_bytes_per_launch": alg},

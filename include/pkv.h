@@ -30,7 +30,7 @@
  *   * dtype is one of PKV_F32, PKV_F16, PKV_BF16; K, V, q, k_new, v_new and out share it.
  *     Arithmetic is fp32 (fp32 products and accumulation), with one exception: where
  *     the weighted sum of V runs on the matrix cores for 16 query columns at once
- *     (multi-query attention, the shared-prefix pass and quantized caches, 16-bit
+ *     (multi-query attention, the shared-prefix tasks and quantized caches, 16-bit
  *     dtypes), the softmax weights (and, for quantized caches, the dequantized V) are
  *     rounded to the dtype first, and the running sum uses the same rounded weights.
  *     Outputs are rounded to the dtype with round-to-nearest-even.
@@ -309,10 +309,11 @@ int32_t pkv_paged_multi_query_step(void* out, const void* q, void* k_pool, void*
  * Source: "LLM推理与服务：面试问题与推荐回答" Q2 and Q3 (sequences share physical blocks of a
  * common prefix, stored once); "Scaling Book 第 11 章" §11.3-§11.4 (prefix caching).
  * The attention computed is exactly that of pkv_paged_decode_attention; the grouping only
- * changes how the shared blocks are read: a prefix pass streams each group's shared blocks
- * once and scores them against the queries of all members (up to 64 (member, head)
- * columns per KV head per workgroup), then the balanced split covers each sequence's own
- * blocks, and the merge kernel combines the two.
+ * changes how the shared blocks are read. One kernel streams everything: its first
+ * workgroups each take one prefix task (a 512-token partition of a group's shared blocks,
+ * read once and scored against the queries of all members, up to 64 (member, head)
+ * columns per KV head) and fewer of the sequences' own blocks, which the balanced split
+ * hands to every workgroup; a merge kernel then combines the two kinds of records.
  *
  *   seq_group        [num_seqs] int32 device: group of each sequence in [0, n_groups), or
  *                    -1 for none.
@@ -325,7 +326,7 @@ int32_t pkv_paged_multi_query_step(void* out, const void* q, void* k_pool, void*
  *                    every member of a group that shares blocks and has more than
  *                    max_group_size members, or more than max_shared_blocks (or
  *                    max_blocks_per_seq) shared blocks.
- *   max_group_size   host bound on members per group (sizes the prefix-pass grid).
+ *   max_group_size   host bound on members per group (sizes the prefix tasks).
  *   max_shared_blocks host bound on group_blocks (sizes the prefix records).
  * Other arguments as pkv_paged_decode_attention (balanced split, num_seqs <= 4096);
  * workspace size from pkv_shared_prefix_workspace_bytes.

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 # (object name, source, extra flags). Host C++ (*.cpp) holds the C ABI, the dtype dispatch
 # and the block manager; the kernels are in *.hip. pkv_decode.hip holds every decode,
-# merge and prefix-pass kernel and is compiled once per dtype.
+# and merge kernel (with the shared-prefix tasks) and is compiled once per dtype.
 UNITS = [
     ("pkv_capi", "pkv_capi.cpp", []),
     ("pkv_dispatch", "pkv_dispatch.cpp", []),
@@ -41,7 +41,7 @@ SOURCES = sorted({src for _, src, _ in UNITS})
 # is written as scalar float code and must lower to unpacked VALU instructions.
 # Matrix-core accumulators are kept in ordinary vector registers (the MFMA VGPR form):
 # the kernels that accumulate P.V on the matrix cores (multi-query, quantized, shared-
-# prefix pass) otherwise shuttle them through the accumulation registers around every
+# prefix tasks) otherwise shuttle them through the accumulation registers around every
 # rescale, which costs 3-10% in those kernels; the other kernels compile the same.
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -39,8 +39,8 @@ struct Plan {
   int64_t parts;         // fixed mode: partitions of the longest sequence
   size_t records;        // partial-result records the workspace must hold
   size_t prefix_ints;    // split mode: block prefix sums
-  size_t shared_records; // shared-prefix pass records
-  int32_t prefix_parts;  // shared-prefix pass partitions
+  size_t shared_records; // shared-prefix task records
+  int32_t prefix_parts;  // shared-prefix task partitions
   size_t flag_ints;      // shared-prefix member flags
   size_t bytes;          // total workspace bytes
 };
@@ -532,7 +532,9 @@ int32_t pkv_paged_decode_attention_shared_prefix(
   if (!workspace || workspace_bytes < plan.bytes || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
   const int32_t g = n_heads / n_kv_heads;
   const int64_t sets = ((int64_t)max_group_size * g + pkv::kPrefixColumns - 1) / pkv::kPrefixColumns;
-  if ((int64_t)n_groups * sets > 65535) return PKV_ERR_SHAPE;   // grid z limit
+  // prefix tasks: at most (partitions x KV heads x column quads x groups)
+  if ((int64_t)plan.prefix_parts * n_kv_heads * sets * n_groups > (int64_t(1) << 24))
+    return PKV_ERR_SHAPE;
 
   pkv::DecodeArgs a{};
   a.out = out;

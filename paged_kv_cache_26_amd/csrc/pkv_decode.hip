@@ -151,7 +151,7 @@ struct Tile {
 // which fit 32 bits (a block is at most 16 * 256 * 128 * 4 bytes), so each load is the
 // scalar-base + 32-bit-offset form and needs no 64-bit address arithmetic per lane.
 // V loads carry the non-temporal hint when each V byte is used once (NT_V); the shared-
-// prefix pass, whose four waves read the same blocks, keeps them cacheable.
+// prefix tasks, whose four waves per KV head read the same blocks, keep them cacheable.
 template <typename T, bool NT>
 __device__ __forceinline__ T load_v(const char* p) {
   if constexpr (NT)
@@ -347,7 +347,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
 // last iterations make it wait for every outstanding load before each fetch; there the
 // wave keeps one block in flight, fetched a whole block ahead. With kDepth = 1 this loop
 // keeps one block in flight too, but without the drains and with the last blocks in a
-// loop of their own; the single-query kernels (one block ahead) and the shared-prefix pass
+// loop of their own; the single-query kernels (one block ahead) and the shared-prefix tasks
 // (kPrefixDepth ahead) run faster with it, the multi-query and quantized kernels do not and
 // keep stream_tiles. `begin()` runs once, right after the first table entry's load is
 // issued.
@@ -527,7 +527,8 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
     slot = sm_new[threadIdx.x >> 6];
     if (has_new) piece = new_rows_load<DT, D>(a, b, j, lane);
   }
-  // the pipelined stream, one block ahead
+  // the pipelined stream, one block ahead (two measured no faster, also for the private
+  // blocks of the shared-prefix launch)
   stream_blocks<DT, D, 1, true, true>(a, b, j, blk_begin, n_my, lane, bad,
                                       [&](Tile<DT, D>& t, int tok0) {
     if constexpr (kAppend)
@@ -1216,7 +1217,8 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, i
       write_final_mq<DT, D, G>(a, st, bad, b, j, lane);
     else
       write_record_mq<DT, D, G>(a, st, bad, lane, rec);
-  } else if constexpr (MODE == kModeSingle || MODE == kModeSingleAppend) {
+  } else if constexpr (MODE == kModeSingle || MODE == kModeSingleAppend ||
+                       MODE == kModeSinglePrefix) {
     WaveState<DT, D, G> st;
     attend<DT, D, G, MODE == kModeSingleAppend>(st, bad, a, b, j, blk_begin, n_my, tok_end,
                                                 n_ctx, lane);
@@ -1259,6 +1261,175 @@ __device__ __forceinline__ bool usable(const DecodeArgs& a, int b, int n_ctx) {
   return valid_len(a, n_ctx) && shared_blocks_of(a, b, n_ctx) >= 0;
 }
 
+// Shares of the balanced split. Workgroup w < W takes the private units [begin(w),
+// begin(w + 1)). Without prefix tasks begin(w) = floor(w T / W): equal shares. With them,
+// workgroups w < Pw run one prefix task first and are given ceff fewer units:
+// begin(w) = floor(w S / W) - ceff * min(w, Pw) with S = T + Pw * ceff, which still ends at
+// begin(W) = T. ceff is capped so that every workgroup keeps at least one unit
+// (floor(S / W) >= ceff + 1), hence the segments of one stream still come from consecutive
+// workgroups. W is at most kSplitMaxWorkgroups (the records are sized for it) and gives
+// each workgroup at least kSplitMinBlocks units.
+struct SplitShares {
+  long long T, W, Pw, ceff, S;
+  __device__ long long begin(long long w) const { return w * S / W - ceff * min(w, Pw); }
+  // the workgroup owning unit x < T: the largest w with begin(w) <= x
+  __device__ long long owner(long long x) const {
+    const long long w2 = ((x + ceff * Pw + 1) * W - 1) / S;   // among w >= Pw
+    if (w2 >= Pw) return w2;
+    return ((x + 1) * W - 1) / (S - ceff * W);                // begin(w) = floor(w (S - ceff W) / W)
+  }
+};
+
+__device__ __forceinline__ SplitShares split_shares(const DecodeArgs& a, long long T, long long grid) {
+  SplitShares x;
+  x.T = T;
+  x.W = min(min(grid, (long long)kSplitMaxWorkgroups), (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
+  x.Pw = min((long long)a.prefix_tasks, x.W);
+  x.ceff = x.W > x.Pw ? max(0LL, min((long long)a.prefix_cost, (T - x.W) / (x.W - x.Pw))) : 0;
+  x.S = T + x.Pw * x.ceff;
+  return x;
+}
+
+// Prefix-pass blocks in flight per wave: K and V of one block take 4 * kNK + 4 * kVW
+// registers per lane; 64 registers go to prefetch (two blocks ahead for 16-bit d 128). On
+// the pipelined stream two blocks ahead measured fastest for the shared-prefix workload:
+// 84.4 us, against 85.4 / 85.6 / 86.7 us at 3 / 4 / 5 and 90.2 us at 8.
+template <int DT, int D>
+constexpr int kPrefixDepth =
+    64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) > 1
+        ? 64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) : 1;
+
+// Shared-prefix task `task` of a split workgroup of NW waves: prefix partition p
+// (kPrefixPartition tokens) of group g, KV heads jp * NW/4 .. and column quad cs4. Wave v
+// takes KV head j = jp * NW/4 + v / 4 and the 16 columns k = (cs4 * 4 + v % 4) * 16 + c
+// (lane column c), column k being the pair (member m = k / G, head h = k % G), members
+// being the sequences of group g in increasing order. Every wave reads its partition's K/V
+// blocks through the first member's table (the four waves of a KV head read the same
+// bytes, so HBM sees them once) and runs them against its query tile with the multi-query
+// block processor (no causal limit: every shared token is visible to every member), then
+// leaves one (m, l, O) record per (member, head) of its columns for partition p. The tasks
+// of KV heads 0.. and column quad 0 also compare every member's table with the first
+// member's over their partition and leave one flag per (member, partition) for the merge.
+// Tasks are numbered head pair fastest, then partition, column quad and group, so the
+// tasks reading one partition's token rows run side by side. Every thread of the
+// workgroup calls it (it has barriers) and returns with no memory traffic pending.
+template <int DT, int D, int G, int NW>
+__device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
+  using G_ = Geo<DT, D>;
+  constexpr int kThreads = 64 * NW;
+  constexpr int kHeadsPerTask = NW / kPrefixWaves;
+  static_assert(kHeadsPerTask >= 1 && NW % kPrefixWaves == 0, "whole KV heads per task");
+  __shared__ int sm_members[kSplitMaxSeqs];
+  __shared__ int sm_flag[kSplitMaxSeqs];
+  __shared__ int sm_wsum[NW];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int B = a.num_seqs;
+  const int HP = (a.n_kv_heads + kHeadsPerTask - 1) / kHeadsPerTask;
+  int t = task;
+  const int jp = t % HP;
+  t /= HP;
+  const int p = t % a.prefix_parts;
+  t /= a.prefix_parts;
+  const int cs4 = t % a.prefix_sets;
+  const int g = t / a.prefix_sets;
+  if (g >= a.n_groups) return;                             // uniform: before any barrier
+
+  const int sb = a.group_blocks[g];
+  if (sb <= 0 || sb > a.max_blocks_per_seq || sb > a.max_shared_blocks) return;
+  constexpr int kPartBlocks = kPrefixPartition / kBlockTokens;
+  const int blk_begin = p * kPartBlocks;
+  const int blk_end = min(sb, blk_begin + kPartBlocks);
+  if (blk_begin >= blk_end) return;
+
+  // Members of g, in sequence order: per-thread counts over a contiguous chunk, an
+  // exclusive scan (waves, then wave totals), scatter.
+  const int chunk = (B + kThreads - 1) / kThreads;
+  const int s0 = min(B, tid * chunk), s1 = min(B, s0 + chunk);
+  int cnt = 0;
+  for (int s = s0; s < s1; ++s) cnt += a.seq_group[s] == g;
+  int incl = cnt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) sm_wsum[wave] = incl;
+  __syncthreads();
+  int pos = incl - cnt, M = 0;
+#pragma unroll
+  for (int v = 0; v < NW; ++v) {
+    const int x = sm_wsum[v];
+    pos += v < wave ? x : 0;
+    M += x;
+  }
+  for (int s = s0; s < s1; ++s)
+    if (a.seq_group[s] == g) sm_members[pos++] = s;
+  __syncthreads();
+  if (M == 0) return;                                      // uniform
+  const int leader = sm_members[0];
+  const int32_t* lead_row = a.block_tables + (size_t)leader * a.max_blocks_per_seq;
+  const bool too_many = M > a.max_group_size;
+
+  if (jp == 0 && cs4 == 0) {        // uniform over the workgroup
+    // one (member, block) pair per thread and step, so the table reads go out together
+    const int nblk = blk_end - blk_begin;
+    for (int m = tid; m < M; m += kThreads) sm_flag[m] = too_many;
+    __syncthreads();
+#pragma unroll 4
+    for (int x = tid; x < M * nblk; x += kThreads) {
+      const int m = x / nblk, k = blk_begin + (x - m * nblk);
+      if (a.block_tables[(size_t)sm_members[m] * a.max_blocks_per_seq + k] != lead_row[k])
+        sm_flag[m] = 1;            // every writer stores the same value
+    }
+    __syncthreads();
+    for (int m = tid; m < M; m += kThreads)
+      a.ws_flags[(size_t)sm_members[m] * a.prefix_parts + p] = sm_flag[m];
+  }
+  const int j = jp * kHeadsPerTask + wave / kPrefixWaves;
+  const int k0 = (cs4 * kPrefixWaves + wave % kPrefixWaves) * 16;   // first column of this wave
+  if (too_many || j >= a.n_kv_heads || k0 >= M * G) return;         // no barrier below
+  const int tok_end = blk_end * kBlockTokens;
+
+  const int k = k0 + c;
+  const bool used = k < M * G;
+  u32x4 qf[G_::kNK];
+  load_query<DT, D>(a, used, used ? (size_t)sm_members[k / G] * a.n_heads + (size_t)j * G + k % G : 0,
+                    r, qf);
+  MqState<DT, D> st;
+  int bad = 0;
+  // The four waves of a KV head read the same blocks, so each keeps more of them in
+  // flight than a decode wave does.
+  stream_blocks<DT, D, kPrefixDepth<DT, D>, false, true>(a, leader, j, blk_begin, blk_end - blk_begin,
+                                                   lane, bad,
+                                            [&](const Tile<DT, D>& tl, int tok0) {
+    if (tok0 + kBlockTokens > tok_end)
+      process_block_mq<DT, D, true>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
+    else
+      process_block_mq<DT, D, false>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
+  });
+  st.l += __shfl_xor(st.l, 16);
+  st.l += __shfl_xor(st.l, 32);
+  if (!used) return;
+  const float qnan = __builtin_nanf("");
+  const int b = sm_members[k / G];
+  const size_t idx = ((size_t)b * a.n_heads + (size_t)j * G + k % G) * a.prefix_parts + p;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float* dst = a.ws_po + idx * D + G_::kEPL * (4 * r + i);
+#pragma unroll
+    for (int e = 0; e < G_::kEPL; e += 4) {
+      const f32x4 x = {bad ? qnan : st.o[e][i], bad ? qnan : st.o[e + 1][i],
+                       bad ? qnan : st.o[e + 2][i], bad ? qnan : st.o[e + 3][i]};
+      *reinterpret_cast<f32x4*>(dst + e) = x;
+    }
+  }
+  if (r == 0) {
+    a.ws_pm[idx] = bad ? qnan : st.m;
+    a.ws_pl[idx] = bad ? qnan : st.l;
+  }
+}
+
 // Fixed partitions: workgroup = NW waves = KV heads hg*NW .. hg*NW+NW-1 of one
 // (partition, sequence); grid (head groups, partitions, sequences).
 template <int DT, int D, int G, int NW, int MODE>
@@ -1293,6 +1464,10 @@ __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
 // a record for merge_kernel. Segments of stream s = hg * num_seqs + b are produced by
 // consecutive workgroups in increasing order of w, so (w + s) names each segment
 // uniquely: the record of its column c (of C = G * q_len) is ((w + s) * NW + wave) * C + c.
+// kModeSinglePrefix (shared prefixes): the units are each sequence's blocks after its
+// group's shared ones, and workgroups w < prefix_tasks first run prefix task w with a
+// correspondingly smaller share (SplitShares), so the prefix tasks, which wait on their
+// block chain more than on HBM, overlap the streaming of the other workgroups.
 template <int DT, int D, int G, int NW, int MODE>
 __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   constexpr int kThreads = 64 * NW;
@@ -1345,18 +1520,21 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   const int HG = (a.n_kv_heads + NW - 1) / NW;
   const int T1 = sm_pref[B];                    // blocks per head group
   const long long T = (long long)T1 * HG;
-  // Workgroups in use: at most W, and at least kSplitMinBlocks blocks each.
-  const long long W = min((long long)gridDim.x, (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
+  const SplitShares sh = split_shares(a, T, gridDim.x);
+  const long long W = sh.W;                     // workgroups with private units
   if (w == 0)
     for (int s = tid; s <= B; s += kThreads) a.ws_prefix[s] = sm_pref[s];
   const int rows_per_seq = a.q_len * a.n_heads;
   for (int s = w; s < B; s += gridDim.x)        // invalid lengths or groups: NaN outputs
     if (!usable(a, s, a.context_lens[s]))
       write_nan_rows<DT, D>(a, (size_t)s * rows_per_seq, rows_per_seq, tid, kThreads);
+  if constexpr (MODE == kModeSinglePrefix) {
+    if (w < a.prefix_tasks) prefix_task<DT, D, G, NW>(a, w);   // uniform over the workgroup
+  }
   if (w >= W) return;
   const int C = G * a.q_len;
-  const long long u1 = (w + 1) * T / W;
-  long long u = w * T / W;
+  const long long u1 = sh.begin(w + 1);
+  long long u = sh.begin(w);
   while (u < u1) {
     const int hg = (int)(u / T1);
     const int rem = (int)(u - (long long)hg * T1);
@@ -1414,12 +1592,11 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     const int HG = (a.n_kv_heads + NW - 1) / NW;
     const int T1 = a.ws_prefix[B];
     const long long T = (long long)T1 * HG;
-    const long long W = min((long long)a.split_workgroups, (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
-    const int nb = a.ws_prefix[b + 1] - a.ws_prefix[b];
+    const SplitShares sh = split_shares(a, T, a.split_workgroups);
+    const int nb = a.ws_prefix[b + 1] - a.ws_prefix[b];      // >= 1 for a usable sequence
     const long long U = (long long)hg * T1 + a.ws_prefix[b];
-    // workgroup owning unit x: the largest w with w*T/W <= x
-    const long long first = ((U + 1) * W - 1) / T;
-    const long long last = ((U + nb) * W - 1) / T;
+    const long long first = sh.owner(U);
+    const long long last = sh.owner(U + nb - 1);
     const int grp = a.seq_group ? a.seq_group[b] : -1;
     if (first == last && grp < 0) return;                   // decode wrote the output
     n_rec = (int)(last - first + 1);
@@ -1434,7 +1611,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
         pbase = ((size_t)b * a.n_heads + h) * a.prefix_parts;
         for (int p = tid; p < n_pre; p += 256) nan_row |= a.ws_flags[(size_t)b * a.prefix_parts + p];
       }
-      // the group broke its promise (see prefix_kernel): NaN row
+      // the group broke its promise (see prefix_task): NaN row
       if (__syncthreads_or(nan_row)) {
         for (int x = tid; x < D; x += 256) store_elem<DT>(a.out, (size_t)row * D + x, __builtin_nanf(""));
         return;
@@ -1529,12 +1706,11 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
     const int HG = (a.n_kv_heads + NW - 1) / NW;
     const int T1 = a.ws_prefix[B];
     const long long T = (long long)T1 * HG;
-    const long long W = min((long long)a.split_workgroups, (T + kSplitMinBlocks - 1) / kSplitMinBlocks);
-    const int nb = a.ws_prefix[b + 1] - a.ws_prefix[b];
+    const SplitShares sh = split_shares(a, T, a.split_workgroups);
+    const int nb = a.ws_prefix[b + 1] - a.ws_prefix[b];      // >= 1 for a usable sequence
     const long long U = (long long)hg * T1 + a.ws_prefix[b];
-    // workgroup owning unit x: the largest w with w*T/W <= x
-    const long long first = ((U + 1) * W - 1) / T;
-    const long long last = ((U + nb) * W - 1) / T;
+    const long long first = sh.owner(U);
+    const long long last = sh.owner(U + nb - 1);
     const int grp = a.seq_group ? a.seq_group[b] : -1;
     if (first == last && grp < 0) return;                   // decode wrote the output
     n_rec = (int)(last - first + 1);
@@ -1608,7 +1784,7 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
     }
     M = mc;
   }
-  // the group broke its promise (see prefix_kernel): NaN row
+  // the group broke its promise (see prefix_task): NaN row
   if (__any(nan_row)) {
     for (int x = lane; x < D; x += 64) store_elem<DT>(a.out, (size_t)row * D + x, __builtin_nanf(""));
     return;
@@ -1618,125 +1794,6 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(DecodeArgs a) {
   for (int e = 0; e < EL; ++e) store_elem<DT>(a.out, (size_t)row * D + EL * lane + e, acc[e] * inv);
 }
 
-
-// Shared-prefix pass. Workgroup = 4 waves on KV head j of prefix partition p
-// (kPrefixPartition tokens) of group g, column set cs; wave w owns the 16 columns
-// k = cs * 64 + 16 * w + c (lane column c), column k being the pair (member m = k / G,
-// head h = k % G), members being the sequences of group g in increasing order. Every wave
-// reads its partition's K/V blocks through the first member's table (the four waves read
-// the same bytes, so HBM sees them once) and runs them against its query tile with the
-// multi-query block processor (no causal limit: every shared token is visible to every
-// member). The workgroups of KV head 0 and column set 0 also compare every member's table
-// with the first member's over their partition and leave one flag per (member, partition)
-// for the merge.
-// Blocks in flight per prefix-pass wave: K and V of one block take 4 * kNK + 4 * kVW
-// registers per lane; 64 registers go to prefetch (two blocks ahead for 16-bit d 128). On
-// the pipelined stream two blocks ahead measured fastest for the shared-prefix workload:
-// 84.4 us, against 85.4 / 85.6 / 86.7 us at 3 / 4 / 5 and 90.2 us at 8.
-template <int DT, int D>
-constexpr int kPrefixDepth =
-    64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) > 1
-        ? 64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) : 1;
-
-template <int DT, int D, int G>
-__global__ __launch_bounds__(256) void prefix_kernel(DecodeArgs a) {
-  using G_ = Geo<DT, D>;
-  const int p = blockIdx.x, j = blockIdx.y;
-  const int g = blockIdx.z / a.prefix_sets, cs = blockIdx.z - g * a.prefix_sets;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane >> 4, c = lane & 15;
-  const int B = a.num_seqs;
-  __shared__ int sm_members[kSplitMaxSeqs];
-  __shared__ int sm_scan[256];
-
-  const int sb = a.group_blocks[g];
-  if (sb <= 0 || sb > a.max_blocks_per_seq || sb > a.max_shared_blocks) return;
-  constexpr int kPartBlocks = kPrefixPartition / kBlockTokens;
-  const int blk_begin = p * kPartBlocks;
-  const int blk_end = min(sb, blk_begin + kPartBlocks);
-  if (blk_begin >= blk_end) return;                        // uniform: before any barrier
-
-  // Members of g, in sequence order (chunked count, prefix sum, scatter).
-  const int chunk = (B + 255) / 256;
-  const int s0 = min(B, tid * chunk), s1 = min(B, s0 + chunk);
-  int cnt = 0;
-  for (int s = s0; s < s1; ++s) cnt += a.seq_group[s] == g;
-  sm_scan[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int v = tid >= off ? sm_scan[tid - off] : 0;
-    __syncthreads();
-    sm_scan[tid] += v;
-    __syncthreads();
-  }
-  int pos = tid > 0 ? sm_scan[tid - 1] : 0;
-  for (int s = s0; s < s1; ++s)
-    if (a.seq_group[s] == g) sm_members[pos++] = s;
-  const int M = sm_scan[255];
-  __syncthreads();
-  if (M == 0) return;
-  const int leader = sm_members[0];
-  const int32_t* lead_row = a.block_tables + (size_t)leader * a.max_blocks_per_seq;
-  const bool too_many = M > a.max_group_size;
-
-  if (j == 0 && cs == 0) {          // uniform over the workgroup
-    // one (member, block) pair per thread and step, so the table reads go out together
-    __shared__ int sm_flag[kSplitMaxSeqs];
-    const int nblk = blk_end - blk_begin;
-    for (int m = tid; m < M; m += 256) sm_flag[m] = too_many;
-    __syncthreads();
-#pragma unroll 4
-    for (int x = tid; x < M * nblk; x += 256) {
-      const int m = x / nblk, k = blk_begin + (x - m * nblk);
-      if (a.block_tables[(size_t)sm_members[m] * a.max_blocks_per_seq + k] != lead_row[k])
-        sm_flag[m] = 1;            // every writer stores the same value
-    }
-    __syncthreads();
-    for (int m = tid; m < M; m += 256)
-      a.ws_flags[(size_t)sm_members[m] * a.prefix_parts + p] = sm_flag[m];
-  }
-  const int k0 = cs * 16 * kPrefixWaves + 16 * wave;       // first column of this wave
-  if (too_many || k0 >= M * G) return;                     // no barrier below
-  const int tok_end = blk_end * kBlockTokens;
-
-  const int k = k0 + c;
-  const bool used = k < M * G;
-  u32x4 qf[G_::kNK];
-  load_query<DT, D>(a, used, used ? (size_t)sm_members[k / G] * a.n_heads + (size_t)j * G + k % G : 0,
-                    r, qf);
-  MqState<DT, D> st;
-  int bad = 0;
-  // The four waves read the same blocks, so each keeps more of them in flight than a
-  // decode wave does.
-  stream_blocks<DT, D, kPrefixDepth<DT, D>, false, true>(a, leader, j, blk_begin, blk_end - blk_begin,
-                                                   lane, bad,
-                                            [&](const Tile<DT, D>& tl, int tok0) {
-    if (tok0 + kBlockTokens > tok_end)
-      process_block_mq<DT, D, true>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
-    else
-      process_block_mq<DT, D, false>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
-  });
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
-  if (!used) return;
-  const float qnan = __builtin_nanf("");
-  const int b = sm_members[k / G];
-  const size_t idx = ((size_t)b * a.n_heads + (size_t)j * G + k % G) * a.prefix_parts + p;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float* dst = a.ws_po + idx * D + G_::kEPL * (4 * r + i);
-#pragma unroll
-    for (int e = 0; e < G_::kEPL; e += 4) {
-      const f32x4 x = {bad ? qnan : st.o[e][i], bad ? qnan : st.o[e + 1][i],
-                       bad ? qnan : st.o[e + 2][i], bad ? qnan : st.o[e + 3][i]};
-      *reinterpret_cast<f32x4*>(dst + e) = x;
-    }
-  }
-  if (r == 0) {
-    a.ws_pm[idx] = bad ? qnan : st.m;
-    a.ws_pl[idx] = bad ? qnan : st.l;
-  }
-}
 
 // Resident workgroups of kernel K on the current device: compute units times the
 // kernel's own occupancy. K is a template argument, so every kernel instantiation keeps
@@ -1766,22 +1823,49 @@ int resident_workgroups(int threads) {
   return n;
 }
 
+// Private units a workgroup gives up for running one prefix task (units: one block of
+// the workgroup's NW KV heads). A task runs kPrefixPartition tokens (32 blocks) of NW / 4
+// KV heads through four waves each, a chain of 32 multi-query blocks per wave. Measured on
+// the shared-prefix workload (bf16, d 128, G 4; attention us warm / cold, same box): with
+// eight-wave workgroups cost 0: 88.8 / 107.5, 12: 79.2 / 97.4, 18: 75.0 / 94.0,
+// 24: 71.6 / 90.5, 32: 76.0 / 97.3; with four-wave workgroups (units of four KV heads)
+// 16-20: 71.0 / 89.8 (the three-launch form: 83.5 / 99.6). The task takes about as long
+// as 24 (eight heads) or 18 (four heads) private units.
+inline int prefix_task_cost(int nw) {
+  return (kPrefixPartition / kBlockTokens) * (nw == 8 ? 12 : 9) / 16;
+}
+
 template <int DT, int D, int G, int NW, int MODE>
 hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
   bool need_merge;
   if (a.split) {
     constexpr auto kernel = decode_split_kernel<DT, D, G, NW, MODE>;
     a.split_workgroups = min(kSplitMaxWorkgroups, resident_workgroups<kernel>(64 * NW));
+    a.prefix_tasks = 0;
+    a.prefix_cost = 0;
+    if constexpr (MODE == kModeSinglePrefix) {
+      // one task per (partition, KV heads of a workgroup, column quad, group); the first
+      // prefix_tasks workgroups run them (the grid grows if there are more tasks than
+      // resident workgroups)
+      const long long heads = (a.n_kv_heads + NW / kPrefixWaves - 1) / (NW / kPrefixWaves);
+      const long long tasks = (long long)a.prefix_parts * heads * a.prefix_sets * a.n_groups;
+      if (tasks > (1 << 24)) return hipErrorInvalidValue;
+      a.prefix_tasks = (int)tasks;
+      a.prefix_cost = prefix_task_cost(NW);
+      a.split_workgroups = max(a.split_workgroups, a.prefix_tasks);
+    }
     if (a.grid_out) {                             // grid query: report, launch nothing
       *a.grid_out = a.split_workgroups;
       return hipSuccess;
     }
     hipLaunchKernelGGL(kernel, dim3(a.split_workgroups), dim3(64 * NW), 0, stream, a);
     need_merge = true;
-  } else {
+  } else if constexpr (MODE != kModeSinglePrefix) {
     const dim3 grid((a.n_kv_heads + NW - 1) / NW, a.max_partitions, a.num_seqs);
     hipLaunchKernelGGL((decode_fixed_kernel<DT, D, G, NW, MODE>), grid, dim3(64 * NW), 0, stream, a);
     need_merge = a.max_partitions > 1;
+  } else {
+    return hipErrorInvalidValue;                  // shared prefixes need the balanced split
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || !need_merge) return e;
@@ -1861,12 +1945,13 @@ hipError_t launch_quant_dtype(const DecodeArgs& a, int fmt, int d_head, int grou
 }
 
 template <int DT, int D, int G>
-hipError_t launch_prefix_typed(DecodeArgs a, hipStream_t stream) {
-  const dim3 pgrid(a.prefix_parts, a.n_kv_heads, a.n_groups * a.prefix_sets);
-  hipLaunchKernelGGL((prefix_kernel<DT, D, G>), pgrid, dim3(64 * kPrefixWaves), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_waves<DT, D, G>(a, stream);      // split pass + merge (a.split == 1)
+hipError_t launch_prefix_typed(const DecodeArgs& a, hipStream_t stream) {
+  // the workgroup shapes of launch_waves: the prefix tasks run inside the split kernel
+  if constexpr (DT != 0 && G <= 4) {
+    if (max_waves_per_workgroup(a.n_kv_heads) == 8)
+      return launch_typed<DT, D, G, 8, kModeSinglePrefix>(a, stream);
+  }
+  return launch_typed<DT, D, G, 4, kModeSinglePrefix>(a, stream);
 }
 
 template <int DT, int D>

@@ -16,9 +16,9 @@ constexpr int kSplitMaxSeqs = 4096;       // split mode keeps the per-sequence p
 constexpr int kSplitMaxWorkgroups = 1024; // upper bound of the split-mode grid
 constexpr int kSplitMinBlocks = 8;        // fewest blocks a split-mode workgroup is given
 constexpr int kMergeRowsWave = 1024;      // from this many output rows on, a wave per row
-constexpr int kPrefixPartition = 512;     // tokens per prefix-pass partition
-constexpr int kPrefixWaves = 4;           // prefix-pass waves per workgroup, 16 columns each
-constexpr int kPrefixColumns = 16 * kPrefixWaves;
+constexpr int kPrefixPartition = 512;     // tokens per prefix-task partition
+constexpr int kPrefixWaves = 4;           // prefix-task waves per KV head, 16 columns each
+constexpr int kPrefixColumns = 16 * kPrefixWaves;   // columns per KV head of one task
 
 // Quantized KV formats (values of the C ABI's kv_format) and the decode kernels' modes.
 constexpr int kKvInt8 = 1;
@@ -29,6 +29,8 @@ constexpr int kModeQuantInt8 = 2;   // one query, INT8 codes + (s, z) per token 
 constexpr int kModeQuantFp8 = 3;    // one query, E4M3 codes + (s, 0) per token and KV head
 constexpr int kModeSingleAppend = 4; // kModeSingle that also appends the new token (k_new)
 constexpr int kModeMultiAppend = 5;  // kModeMulti that also appends the q_len new tokens
+constexpr int kModeSinglePrefix = 6; // kModeSingle whose first workgroups also run the
+                                     // shared-prefix tasks
 
 // Waves per decode workgroup (one KV head each) used with this many KV heads. The
 // launcher may use fewer (4) for kernels that do not fit 256 registers per lane; this is
@@ -78,12 +80,15 @@ struct DecodeArgs {
   int32_t split_workgroups;          // split mode: grid size W (set by the launcher)
   // Shared prefixes (optional, split mode, q_len 1): seq_group[b] is the group of
   // sequence b (-1: none); the members of group g share their first group_blocks[g]
-  // table entries. The prefix pass reads those blocks once per group and leaves records
-  // ws_p* at (b * n_heads + h) * prefix_parts + p; the split pass covers the rest.
+  // table entries. The prefix tasks read those blocks once per group and leave records
+  // ws_p* at (b * n_heads + h) * prefix_parts + p; the private units cover the rest.
   const int32_t* seq_group;
   const int32_t* group_blocks;
   int32_t n_groups, prefix_parts, prefix_sets;
-  int32_t max_group_size, max_shared_blocks;  // host bounds the prefix grid was sized for
+  int32_t max_group_size, max_shared_blocks;  // host bounds the prefix tasks were sized for
+  // Split mode with shared prefixes: workgroups 0 .. prefix_tasks - 1 each run one prefix
+  // task first and are given prefix_cost fewer private blocks (set by the launcher).
+  int32_t prefix_tasks, prefix_cost;
   float* ws_pm;
   float* ws_pl;
   float* ws_po;
@@ -132,7 +137,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int d_head, int group,
 // Decode over 8-bit codes (dtype 1 or 2 for q / out).
 hipError_t launch_decode_quantized(const DecodeArgs& a, int dtype, int kv_format, int d_head,
                                    int group, hipStream_t stream);
-// Shared-prefix decode (split mode, q_len 1): prefix pass, split pass, merge.
+// Shared-prefix decode (split mode, q_len 1): split kernel with the prefix tasks, merge.
 hipError_t launch_shared_prefix(const DecodeArgs& a, int dtype, int d_head, int group,
                                 hipStream_t stream);
 

@@ -75,7 +75,7 @@ PATHS = {
     "test_gpu_limits": "single-query: fp32 weights, P.V on the vector ALU",
     "test_gpu_multi_query": "multi-query: weights rounded to the dtype, P.V on the matrix cores",
     "test_gpu_mq_step": "multi-query: weights rounded to the dtype, P.V on the matrix cores",
-    "test_gpu_shared_prefix": "shared prefix: prefix pass with weights rounded to the dtype on "
+    "test_gpu_shared_prefix": "shared prefix: prefix tasks with weights rounded to the dtype on "
                               "the matrix cores, private blocks in fp32",
     "test_gpu_quant": "8-bit cache: weights (times the V scale for bf16) rounded to the dtype, "
                       "P.V on the matrix cores",
