@@ -87,6 +87,35 @@ def test_shared_prefix_shapes(dtype, H, Hkv, d, B, groups, prefix):
     assert_close(got, oracle_out(wl), dtype, "shapes")
 
 
+def test_more_prefix_tasks_than_resident_workgroups():
+    """128 groups of 2 over a 1100-token prefix: 3 partitions x 4 KV-head pairs x 128
+    groups = 1536 prefix tasks, more than the split kernel's resident workgroups (the grid
+    grows to one workgroup per task) and more than the workgroups that get private blocks
+    (which then all run tasks as well, with equal shares). Every output against the
+    oracle."""
+    _log("shared prefix: 1536 prefix tasks")
+    wl = sp_workload(B=256, groups=128, prefix=1100, suffix=(5, 60), seed=11)
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    assert grp.n_groups == 128 and grp.max_shared_blocks >= 65
+    got, _ = gpu_shared(wl, grp)
+    assert_close(got, oracle_out(wl), "bf16", "many tasks")
+
+
+def test_prefix_task_share_capped_by_the_private_blocks():
+    """4 groups of 16 over a 2048-token prefix (64 prefix tasks) with short private parts
+    (300-450 tokens, about 1560 private blocks over 195 workgroups): the private units a
+    task workgroup gives up are capped so every workgroup keeps at least one. Every output
+    against the oracle, and repeated calls bitwise identical."""
+    _log("shared prefix: capped task share")
+    wl = sp_workload(B=64, groups=4, prefix=2048, suffix=(300, 450), seed=12)
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    assert grp.n_groups == 4
+    got, t = gpu_shared(wl, grp)
+    assert_close(got, oracle_out(wl), "bf16", "capped share")
+    again, _ = gpu_shared(wl, grp, t=t)
+    assert np.array_equal(got, again)
+
+
 def test_mixed_batch_grouped_and_ungrouped():
     """Sequences outside any group, a group sharing no whole block and a regular group in
     one batch."""
