@@ -531,7 +531,9 @@ int32_t pkv_paged_decode_attention_shared_prefix(
                               max_shared_blocks);
   if (!workspace || workspace_bytes < plan.bytes || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
   const int32_t g = n_heads / n_kv_heads;
-  const int64_t sets = ((int64_t)max_group_size * g + pkv::kPrefixColumns - 1) / pkv::kPrefixColumns;
+  // column sets of 16 (member, head) pairs, taken wph at a time by the waves of a KV head
+  const int wph = pkv::prefix_waves_per_head(max_group_size, g);
+  const int64_t sets = (((int64_t)max_group_size * g + 15) / 16 + wph - 1) / wph;
   // prefix tasks: at most (partitions x KV heads x column quads x groups)
   if ((int64_t)plan.prefix_parts * n_kv_heads * sets * n_groups > (int64_t(1) << 24))
     return PKV_ERR_SHAPE;
@@ -557,6 +559,7 @@ int32_t pkv_paged_decode_attention_shared_prefix(
   a.n_groups = n_groups;
   a.prefix_parts = plan.prefix_parts;
   a.prefix_sets = (int32_t)sets;
+  a.prefix_wph = wph;
   a.max_group_size = max_group_size;
   a.max_shared_blocks = max_shared_blocks;
   char* ws = static_cast<char*>(workspace);

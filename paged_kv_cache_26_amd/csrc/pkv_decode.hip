@@ -1295,42 +1295,45 @@ __device__ __forceinline__ SplitShares split_shares(const DecodeArgs& a, long lo
   return x;
 }
 
-// Prefix-pass blocks in flight per wave: K and V of one block take 4 * kNK + 4 * kVW
+// Prefix-task blocks in flight per wave: K and V of one block take 4 * kNK + 4 * kVW
 // registers per lane; 64 registers go to prefetch (two blocks ahead for 16-bit d 128). On
-// the pipelined stream two blocks ahead measured fastest for the shared-prefix workload:
-// 84.4 us, against 85.4 / 85.6 / 86.7 us at 3 / 4 / 5 and 90.2 us at 8.
+// the pipelined stream two blocks ahead measured fastest for the shared-prefix workload
+// (with the prefix work then in a kernel of its own): 84.4 us, against 85.4 / 85.6 /
+// 86.7 us at 3 / 4 / 5 and 90.2 us at 8.
 template <int DT, int D>
 constexpr int kPrefixDepth =
     64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) > 1
         ? 64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) : 1;
 
 // Shared-prefix task `task` of a split workgroup of NW waves: prefix partition p
-// (kPrefixPartition tokens) of group g, KV heads jp * NW/4 .. and column quad cs4. Wave v
-// takes KV head j = jp * NW/4 + v / 4 and the 16 columns k = (cs4 * 4 + v % 4) * 16 + c
-// (lane column c), column k being the pair (member m = k / G, head h = k % G), members
-// being the sequences of group g in increasing order. Every wave reads its partition's K/V
-// blocks through the first member's table (the four waves of a KV head read the same
-// bytes, so HBM sees them once) and runs them against its query tile with the multi-query
+// (kPrefixPartition tokens) of group g, KV heads jp * NW/wph .. and column-set group cs4,
+// with wph = prefix_wph waves per KV head (enough 16-column sets for the largest group's
+// columns, up to four). Wave v takes KV head j = jp * NW/wph + v / wph and the 16 columns
+// k = (cs4 * wph + v % wph) * 16 + c (lane column c), column k being the pair (member
+// m = k / G, head h = k % G), members being the sequences of group g in increasing order.
+// Every wave reads its partition's K/V blocks through the first member's table (the waves
+// of a KV head read the same bytes, so HBM sees them once) and runs them against its query tile with the multi-query
 // block processor (no causal limit: every shared token is visible to every member), then
 // leaves one (m, l, O) record per (member, head) of its columns for partition p. The tasks
-// of KV heads 0.. and column quad 0 also compare every member's table with the first
+// of KV-head set 0 and column-set group 0 also compare every member's table with the first
 // member's over their partition and leave one flag per (member, partition) for the merge.
-// Tasks are numbered head pair fastest, then partition, column quad and group, so the
-// tasks reading one partition's token rows run side by side. Every thread of the
-// workgroup calls it (it has barriers) and returns with no memory traffic pending.
+// Tasks are numbered KV-head set fastest, then partition, column-set group and group, so
+// the tasks reading one partition's token rows run side by side. Every thread of the
+// workgroup calls it (it has barriers); no barrier follows its record stores.
 template <int DT, int D, int G, int NW>
 __device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
   using G_ = Geo<DT, D>;
   constexpr int kThreads = 64 * NW;
-  constexpr int kHeadsPerTask = NW / kPrefixWaves;
-  static_assert(kHeadsPerTask >= 1 && NW % kPrefixWaves == 0, "whole KV heads per task");
+  static_assert(NW % kPrefixWaves == 0, "whole KV heads per task");
+  const int wph = a.prefix_wph;                 // 1, 2 or 4: divides NW
+  const int heads_per_task = NW / wph;
   __shared__ int sm_members[kSplitMaxSeqs];
   __shared__ int sm_flag[kSplitMaxSeqs];
   __shared__ int sm_wsum[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int B = a.num_seqs;
-  const int HP = (a.n_kv_heads + kHeadsPerTask - 1) / kHeadsPerTask;
+  const int HP = (a.n_kv_heads + heads_per_task - 1) / heads_per_task;
   int t = task;
   const int jp = t % HP;
   t /= HP;
@@ -1391,8 +1394,8 @@ __device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
     for (int m = tid; m < M; m += kThreads)
       a.ws_flags[(size_t)sm_members[m] * a.prefix_parts + p] = sm_flag[m];
   }
-  const int j = jp * kHeadsPerTask + wave / kPrefixWaves;
-  const int k0 = (cs4 * kPrefixWaves + wave % kPrefixWaves) * 16;   // first column of this wave
+  const int j = jp * heads_per_task + wave / wph;
+  const int k0 = (cs4 * wph + wave % wph) * 16;                     // first column of this wave
   if (too_many || j >= a.n_kv_heads || k0 >= M * G) return;         // no barrier below
   const int tok_end = blk_end * kBlockTokens;
 
@@ -1403,8 +1406,8 @@ __device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
                     r, qf);
   MqState<DT, D> st;
   int bad = 0;
-  // The four waves of a KV head read the same blocks, so each keeps more of them in
-  // flight than a decode wave does.
+  // The waves of a KV head read the same blocks, so each keeps more of them in flight
+  // than a decode wave does.
   stream_blocks<DT, D, kPrefixDepth<DT, D>, false, true>(a, leader, j, blk_begin, blk_end - blk_begin,
                                                    lane, bad,
                                             [&](const Tile<DT, D>& tl, int tok0) {
@@ -1829,8 +1832,8 @@ int resident_workgroups(int threads) {
 }
 
 // Private units a workgroup gives up for running one prefix task (units: one block of
-// the workgroup's NW KV heads). A task runs kPrefixPartition tokens (32 blocks) of NW / 4
-// KV heads through four waves each, a chain of 32 multi-query blocks per wave. Measured on
+// the workgroup's NW KV heads). A task runs kPrefixPartition tokens (32 blocks) through
+// every wave, a chain of 32 multi-query blocks per wave. Measured on
 // the shared-prefix workload (bf16, d 128, G 4; attention us warm / cold, same box): with
 // eight-wave workgroups cost 0: 88.8 / 107.5, 12: 79.2 / 97.4, 18: 75.0 / 94.0,
 // 24: 71.6 / 90.5, 32: 76.0 / 97.3; with four-wave workgroups (units of four KV heads)
@@ -1852,7 +1855,8 @@ hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
       // one task per (partition, KV heads of a workgroup, column quad, group); the first
       // prefix_tasks workgroups run them (the grid grows if there are more tasks than
       // resident workgroups)
-      const long long heads = (a.n_kv_heads + NW / kPrefixWaves - 1) / (NW / kPrefixWaves);
+      const int hpt = NW / a.prefix_wph;
+      const long long heads = (a.n_kv_heads + hpt - 1) / hpt;
       const long long tasks = (long long)a.prefix_parts * heads * a.prefix_sets * a.n_groups;
       if (tasks > (1 << 24)) return hipErrorInvalidValue;
       a.prefix_tasks = (int)tasks;

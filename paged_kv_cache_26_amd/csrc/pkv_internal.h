@@ -17,8 +17,14 @@ constexpr int kSplitMaxWorkgroups = 1024; // upper bound of the split-mode grid
 constexpr int kSplitMinBlocks = 8;        // fewest blocks a split-mode workgroup is given
 constexpr int kMergeRowsWave = 1024;      // from this many output rows on, a wave per row
 constexpr int kPrefixPartition = 512;     // tokens per prefix-task partition
-constexpr int kPrefixWaves = 4;           // prefix-task waves per KV head, 16 columns each
-constexpr int kPrefixColumns = 16 * kPrefixWaves;   // columns per KV head of one task
+constexpr int kPrefixWaves = 4;           // most prefix-task waves per KV head, 16 columns each
+
+// Waves per KV head of a prefix task: enough 16-column sets for the largest group's
+// (member, head) columns, rounded up to a power of two, at most kPrefixWaves.
+inline int prefix_waves_per_head(long long max_group_size, int group) {
+  const long long sets = (max_group_size * group + 15) / 16;
+  return sets >= 3 ? kPrefixWaves : (sets == 2 ? 2 : 1);
+}
 
 // Quantized KV formats (values of the C ABI's kv_format) and the decode kernels' modes.
 constexpr int kKvInt8 = 1;
@@ -89,6 +95,7 @@ struct DecodeArgs {
   // Split mode with shared prefixes: workgroups 0 .. prefix_tasks - 1 each run one prefix
   // task first and are given prefix_cost fewer private blocks (set by the launcher).
   int32_t prefix_tasks, prefix_cost;
+  int32_t prefix_wph;                // waves per KV head in a prefix task (1, 2 or 4)
   float* ws_pm;
   float* ws_pl;
   float* ws_po;
