@@ -77,6 +77,7 @@ def test_shared_prefix_small_workload():
     ("bf16", 64, 8, 128, 36, 2, 100),      # 18 members x 8 heads: three column sets
     ("f32", 8, 2, 128, 10, 2, 160),        # fp32, two query tiles per wave
     ("f32", 8, 4, 64, 9, 3, 48),
+    ("bf16", 16, 8, 128, 32, 2, 300),      # 16 members x 2 heads: two waves per KV head
 ])
 def test_shared_prefix_shapes(dtype, H, Hkv, d, B, groups, prefix):
     _log(f"shared prefix: {dtype} H{H} Hkv{Hkv} d{d} B{B} groups{groups} prefix{prefix}")
