@@ -1295,7 +1295,8 @@ __device__ __forceinline__ SplitShares split_shares(const DecodeArgs& a, long lo
   return x;
 }
 
-// Prefix-task blocks in flight per wave: K and V of one block take 4 * kNK + 4 * kVW
+// Prefix-task blocks in flight per wave on the register stream (fp32, or fewer than four
+// waves per KV head): K and V of one block take 4 * kNK + 4 * kVW
 // registers per lane; 64 registers go to prefetch (two blocks ahead for 16-bit d 128). On
 // the pipelined stream two blocks ahead measured fastest for the shared-prefix workload
 // (with the prefix work then in a kernel of its own): 84.4 us, against 85.4 / 85.6 /
@@ -1305,21 +1306,153 @@ constexpr int kPrefixDepth =
     64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) > 1
         ? 64 / (4 * Geo<DT, D>::kNK + 4 * Geo<DT, D>::kVW) : 1;
 
+// Blocks in flight per KV head in the staged prefix stream (four and six measured the same
+// on the shared-prefix workload; four take fewer registers).
+constexpr int kPrefixStage = 4;
+
+// Whether a prefix task streams its blocks through prefix_stream_staged: four waves per KV
+// head and a 16-bit dtype. The fp32 d 128 kernel already runs one wave per SIMD, and the
+// staged stream made its shared-prefix attention slower (86.3 / 100.1 against 77.7 / 94.7
+// us warm / cold on the 8 x 16-sequence batch, 16 / 4 heads); every 16-bit shape measured
+// the same or faster.
+inline __host__ __device__ bool prefix_staged(int dt, int wph) {
+  return dt != 0 && wph == kPrefixWaves;
+}
+
+// s_barrier after this wave's LDS stores have completed, without the workgroup-scope
+// fence of __syncthreads() (which also waits for every outstanding global load).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Staged stream of a prefix task with four waves per KV head: wave q of a head loads rows
+// 4q .. 4q + 3 of K and V of each block (16-byte chunks) into a register ring kPrefixStage
+// blocks deep, stores them into the head's LDS double buffer, and after one barrier per
+// block every wave of the head reads the whole tile from LDS in load_tile's layout. So
+// each block is loaded once per KV head instead of once per wave, and kPrefixStage blocks
+// stay in flight per head for 8 registers per lane each (a whole tile in registers takes
+// 32). K rows are stored with their 16-byte chunks permuted by the row index
+// (chunk ^ row), so the K operand reads (one chunk of 16 rows per lane group) spread over
+// the banks. Every wave of the workgroup runs the same number of iterations (the
+// barrier); head_ok false: the wave's head does not exist (its loads read head 0 and
+// nobody reads its buffer).
+template <int DT, int D, int NW, typename F>
+__device__ __forceinline__ void prefix_stream_staged(const DecodeArgs& a, int b, int j,
+                                                     bool head_ok, int blk_begin, int n_my,
+                                                     int lane, int& bad, F&& process) {
+  using G_ = Geo<DT, D>;
+  constexpr int kCpr = G_::kRow / 16;               // 16-byte chunks per token row
+  constexpr int kWaveChunks = 4 * kCpr;             // four rows
+  constexpr int kPer = (kWaveChunks + 63) / 64;     // chunks per lane and block
+  constexpr int kSwz = kCpr < 16 ? kCpr - 1 : 15;
+  constexpr int S = kPrefixStage;
+  constexpr int NB = S;
+  static_assert(kPrefixPartition / kBlockTokens <= 64, "one table entry per lane");
+  __shared__ u32x4 ring[NW / 4][2][2][16 * kCpr];   // [head][buffer][K, V][chunk]
+  const int wave = threadIdx.x >> 6, q = wave & 3, hs = wave >> 2;
+  const int r = lane >> 4, c = lane & 15;
+  const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;
+  const size_t blk_stride = (size_t)tok_stride * kBlockTokens;
+  const uint32_t head_off = (uint32_t)(head_ok ? j : 0) * G_::kRow;
+  // Every lane loads and stores unconditionally (branches around the loads would make
+  // the compiler wait for all of them): with fewer chunks than lanes the upper lanes
+  // repeat the lower ones' chunks, and a wave whose head does not exist reads head 0.
+  uint32_t goff[kPer];
+  int kdst[kPer], vdst[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int x = (lane + 64 * i) % kWaveChunks;
+    const int row = 4 * q + x / kCpr, ch = x % kCpr;
+    goff[i] = head_off + (uint32_t)row * tok_stride + 16u * ch;
+    kdst[i] = row * kCpr + (ch ^ (row & kSwz));
+    vdst[i] = row * kCpr + ch;
+  }
+  // the partition's table entries, lane i holding block i's (n_my <= 64), loaded before any
+  // tile so that reading them never waits for tile loads
+  const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_begin;
+  const int tbl = lane < n_my ? trow[lane] : 0;
+  u32x4 rk[NB][kPer], rv[NB][kPer];
+  auto fetch = [&](int s, int i) {
+    const int pb = __builtin_amdgcn_readlane(tbl, i);
+    const bool ok = (unsigned)pb < (unsigned)a.num_blocks;
+    bad |= !ok;
+    const char* kb = a.k_pool + (size_t)(ok ? pb : 0) * blk_stride;
+    const char* vb = a.v_pool + (size_t)(ok ? pb : 0) * blk_stride;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      rk[s][i] = *reinterpret_cast<const u32x4*>(kb + goff[i]);
+      rv[s][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vb + goff[i]));
+    }
+  };
+  auto step = [&](int s, int i, bool refill) {
+    const int buf = i & 1;
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      ring[hs][buf][0][kdst[k]] = rk[s][k];
+      ring[hs][buf][1][vdst[k]] = rv[s][k];
+    }
+    if (refill) fetch(s, i + S);
+    lds_barrier();
+    Tile<DT, D> t;
+    const u32x4* kr = ring[hs][buf][0];
+#pragma unroll
+    for (int kk = 0; kk < G_::kNK; ++kk) t.k[kk] = kr[c * kCpr + ((4 * kk + r) ^ (c & kSwz))];
+    const unsigned* vr = reinterpret_cast<const unsigned*>(ring[hs][buf][1]);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const unsigned* src = vr + (4 * r + jj) * (G_::kRow / 4) + c * G_::kVW;
+      if constexpr (G_::kVW == 8) {
+        const u32x4 a0 = reinterpret_cast<const u32x4*>(src)[0], a1 = reinterpret_cast<const u32x4*>(src)[1];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) { t.v[jj][x] = a0[x]; t.v[jj][4 + x] = a1[x]; }
+      } else if constexpr (G_::kVW == 4) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) t.v[jj][x] = a0[x];
+      } else {
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(src);
+        t.v[jj][0] = a0[0];
+        t.v[jj][1] = a0[1];
+      }
+    }
+    process(t, (blk_begin + i) * kBlockTokens);
+  };
+  // a partition shorter than S blocks loads its last block again instead of skipping loads
+#pragma unroll
+  for (int d0 = 0; d0 < S; ++d0) fetch(d0, min(d0, n_my - 1));
+  const int n_fetching = n_my - S;          // iterations i < n_fetching refill block i + S
+  int i0 = 0;
+  for (; i0 + NB <= n_fetching; i0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) step(u, i0 + u, true);
+  }
+  for (; i0 < n_my; i0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int i = i0 + u;
+      if (i >= n_my) break;
+      step(u, i, i < n_fetching);
+    }
+  }
+}
+
 // Shared-prefix task `task` of a split workgroup of NW waves: prefix partition p
 // (kPrefixPartition tokens) of group g, KV heads jp * NW/wph .. and column-set group cs4,
 // with wph = prefix_wph waves per KV head (enough 16-column sets for the largest group's
 // columns, up to four). Wave v takes KV head j = jp * NW/wph + v / wph and the 16 columns
 // k = (cs4 * wph + v % wph) * 16 + c (lane column c), column k being the pair (member
 // m = k / G, head h = k % G), members being the sequences of group g in increasing order.
-// Every wave reads its partition's K/V blocks through the first member's table (the waves
-// of a KV head read the same bytes, so HBM sees them once) and runs them against its query tile with the multi-query
-// block processor (no causal limit: every shared token is visible to every member), then
+// Every wave reads its partition's K/V blocks through the first member's table and runs
+// them against its query tile with the multi-query block processor (no causal limit: every shared token is visible to every member), then
 // leaves one (m, l, O) record per (member, head) of its columns for partition p. The tasks
 // of KV-head set 0 and column-set group 0 also compare every member's table with the first
 // member's over their partition and leave one flag per (member, partition) for the merge.
 // Tasks are numbered KV-head set fastest, then partition, column-set group and group, so
 // the tasks reading one partition's token rows run side by side. Every thread of the
-// workgroup calls it (it has barriers); no barrier follows its record stores.
+// workgroup calls it (it has barriers); no barrier follows its record stores. With four
+// waves per KV head and a 16-bit dtype the blocks come through prefix_stream_staged (one
+// load per head); otherwise each wave streams them itself (the register stream,
+// kPrefixDepth ahead; the waves of a head read the same bytes, so HBM sees them once).
 template <int DT, int D, int G, int NW>
 __device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
   using G_ = Geo<DT, D>;
@@ -1396,26 +1529,39 @@ __device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
   }
   const int j = jp * heads_per_task + wave / wph;
   const int k0 = (cs4 * wph + wave % wph) * 16;                     // first column of this wave
-  if (too_many || j >= a.n_kv_heads || k0 >= M * G) return;         // no barrier below
   const int tok_end = blk_end * kBlockTokens;
-
   const int k = k0 + c;
   const bool used = k < M * G;
   u32x4 qf[G_::kNK];
-  load_query<DT, D>(a, used, used ? (size_t)sm_members[k / G] * a.n_heads + (size_t)j * G + k % G : 0,
-                    r, qf);
   MqState<DT, D> st;
   int bad = 0;
-  // The waves of a KV head read the same blocks, so each keeps more of them in flight
-  // than a decode wave does.
-  stream_blocks<DT, D, kPrefixDepth<DT, D>, false, true>(a, leader, j, blk_begin, blk_end - blk_begin,
-                                                   lane, bad,
-                                            [&](const Tile<DT, D>& tl, int tok0) {
+  auto proc = [&](const Tile<DT, D>& tl, int tok0) {
     if (tok0 + kBlockTokens > tok_end)
       process_block_mq<DT, D, true>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
     else
       process_block_mq<DT, D, false>(st, tl, qf, tok0, tok_end, tok_end, tok_end, a.scale_log2, r);
-  });
+  };
+  if (prefix_staged(DT, wph)) {       // uniform: the staged stream, barriers per block
+    if (too_many) return;
+    const bool head_ok = j < a.n_kv_heads;
+    const bool active = head_ok && k0 < M * G;   // waves without columns still load
+    load_query<DT, D>(a, used && active,
+                      used && active ? (size_t)sm_members[k / G] * a.n_heads + (size_t)j * G + k % G : 0,
+                      r, qf);
+    prefix_stream_staged<DT, D, NW>(a, leader, j, head_ok, blk_begin, blk_end - blk_begin, lane,
+                                    bad, [&](const Tile<DT, D>& tl, int tok0) {
+      if (active) proc(tl, tok0);
+    });
+    if (!active) return;                         // no barrier below
+  } else {
+    if (too_many || j >= a.n_kv_heads || k0 >= M * G) return;       // no barrier below
+    load_query<DT, D>(a, used, used ? (size_t)sm_members[k / G] * a.n_heads + (size_t)j * G + k % G : 0,
+                      r, qf);
+    // The waves of a KV head read the same blocks, so each keeps more of them in flight
+    // than a decode wave does.
+    stream_blocks<DT, D, kPrefixDepth<DT, D>, false, true>(a, leader, j, blk_begin,
+                                                           blk_end - blk_begin, lane, bad, proc);
+  }
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
   if (!used) return;
@@ -1833,13 +1979,17 @@ int resident_workgroups(int threads) {
 
 // Private units a workgroup gives up for running one prefix task (units: one block of
 // the workgroup's NW KV heads). A task runs kPrefixPartition tokens (32 blocks) through
-// every wave, a chain of 32 multi-query blocks per wave. Measured on
-// the shared-prefix workload (bf16, d 128, G 4; attention us warm / cold, same box): with
-// eight-wave workgroups cost 0: 88.8 / 107.5, 12: 79.2 / 97.4, 18: 75.0 / 94.0,
-// 24: 71.6 / 90.5, 32: 76.0 / 97.3; with four-wave workgroups (units of four KV heads)
-// 16-20: 71.0 / 89.8 (the three-launch form: 83.5 / 99.6). The task takes about as long
-// as 24 (eight heads) or 18 (four heads) private units.
-inline int prefix_task_cost(int nw) {
+// every wave, a chain of 32 multi-query blocks per wave. Measured on the shared-prefix
+// workload (bf16, d 128, G 4, four waves per KV head; attention us warm / cold, same box).
+// Register stream: eight-wave workgroups cost 0: 88.8 / 107.5, 12: 79.2 / 97.4,
+// 18: 75.0 / 94.0, 24: 71.6 / 90.5, 32: 76.0 / 97.3; four-wave workgroups (units of four
+// KV heads) 16-20: 71.0 / 89.8. Staged stream (prefix_stream_staged, same box: register
+// stream at 24 72.2 / 91.1): eight-wave workgroups 12: 71.8 / 87.7, 16: 69.0 / 85.2,
+// 20: 69.4 / 87.6, 24: 71.6 / 89.0; four-wave workgroups 16: 69.7 / 85.7, 24: 70.1 / 86.4,
+// 32: 76.4 / 94.7. So a staged task takes about as long as 16 private units, a register-
+// stream task about 24 (eight heads) or 18 (four).
+inline int prefix_task_cost(int dt, int nw, int wph) {
+  if (prefix_staged(dt, wph)) return kPrefixPartition / kBlockTokens / 2;
   return (kPrefixPartition / kBlockTokens) * (nw == 8 ? 12 : 9) / 16;
 }
 
@@ -1860,7 +2010,7 @@ hipError_t launch_typed(DecodeArgs a, hipStream_t stream) {
       const long long tasks = (long long)a.prefix_parts * heads * a.prefix_sets * a.n_groups;
       if (tasks > (1 << 24)) return hipErrorInvalidValue;
       a.prefix_tasks = (int)tasks;
-      a.prefix_cost = prefix_task_cost(NW);
+      a.prefix_cost = prefix_task_cost(DT, NW, a.prefix_wph);
       a.split_workgroups = max(a.split_workgroups, a.prefix_tasks);
     }
     if (a.grid_out) {                             // grid query: report, launch nothing

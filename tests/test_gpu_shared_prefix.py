@@ -78,6 +78,12 @@ def test_shared_prefix_small_workload():
     ("f32", 8, 2, 128, 10, 2, 160),        # fp32, two query tiles per wave
     ("f32", 8, 4, 64, 9, 3, 48),
     ("bf16", 16, 8, 128, 32, 2, 300),      # 16 members x 2 heads: two waves per KV head
+    # four waves per KV head: 16-bit types stage each block through LDS (the f16 d 64 row
+    # above too: half the lanes repeat a chunk), fp32 streams it per wave
+    ("f32", 16, 4, 128, 24, 2, 400),
+    ("f32", 16, 4, 64, 24, 2, 230),
+    ("bf16", 32, 8, 128, 24, 2, 40),       # two shared blocks, fewer than the blocks in flight
+    ("f16", 32, 8, 128, 24, 2, 900),       # two partitions, the second one 24 blocks
 ])
 def test_shared_prefix_shapes(dtype, H, Hkv, d, B, groups, prefix):
     _log(f"shared prefix: {dtype} H{H} Hkv{Hkv} d{d} B{B} groups{groups} prefix{prefix}")
