@@ -893,6 +893,15 @@ __device__ __forceinline__ void codes_to_f32(unsigned w, float& x0, float& x1) {
 }
 
 // Two fp32 values rounded (to nearest even) into one word of the 16-bit type DT.
+// Two FP8 codes (bytes 2H, 2H + 1 of w) as a packed bf16 pair, low half first, with
+// gfx950's v_cvt_scalef32_pk_bf16_fp8 at scale 1: every E4M3 value is exact in bf16, and
+// the instruction decodes all 256 bytes bitwise as v_cvt_pk_f32_fp8 followed by rounding
+// to bf16 (checked on the GPU), in one instruction instead of two.
+template <int H>
+__device__ __forceinline__ unsigned fp8_pair_bf16(unsigned w) {
+  return __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, H != 0));
+}
+
 template <int DT>
 __device__ __forceinline__ unsigned pack16(float x0, float x1) {
   if constexpr (DT == 2) {
@@ -978,13 +987,19 @@ __device__ __forceinline__ void process_block_q(QState<DT, D>& st, const QTile<D
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     const unsigned w0 = t.k[kk >> 1][(kk & 1) * 2], w1 = t.k[kk >> 1][(kk & 1) * 2 + 1];
-    float x[8];
-    codes_to_f32<FMT, 0>(w0, x[0], x[1]);
-    codes_to_f32<FMT, 1>(w0, x[2], x[3]);
-    codes_to_f32<FMT, 0>(w1, x[4], x[5]);
-    codes_to_f32<FMT, 1>(w1, x[6], x[7]);
-    const u32x4 a16 = {pack16<DT>(x[0], x[1]), pack16<DT>(x[2], x[3]), pack16<DT>(x[4], x[5]),
-                       pack16<DT>(x[6], x[7])};
+    u32x4 a16;
+    if constexpr (FMT == kKvFp8 && DT == 2) {
+      a16 = u32x4{fp8_pair_bf16<0>(w0), fp8_pair_bf16<1>(w0), fp8_pair_bf16<0>(w1),
+                  fp8_pair_bf16<1>(w1)};
+    } else {
+      float x[8];
+      codes_to_f32<FMT, 0>(w0, x[0], x[1]);
+      codes_to_f32<FMT, 1>(w0, x[2], x[3]);
+      codes_to_f32<FMT, 0>(w1, x[4], x[5]);
+      codes_to_f32<FMT, 1>(w1, x[6], x[7]);
+      a16 = u32x4{pack16<DT>(x[0], x[1]), pack16<DT>(x[2], x[3]), pack16<DT>(x[4], x[5]),
+                  pack16<DT>(x[6], x[7])};
+    }
     acc = mfma32<DT>(a16, qf[kk], acc);
   }
   const float sk[4] = {row_bcast<0>(t.sc), row_bcast<2>(t.sc), row_bcast<4>(t.sc), row_bcast<6>(t.sc)};
@@ -1037,18 +1052,40 @@ __device__ __forceinline__ void process_block_q(QState<DT, D>& st, const QTile<D
 #pragma unroll
       for (int x = 0; x < VW; ++x)            // codes of unused slots may decode to NaN
         vw[jj][x] = (!tail || tok0 + jj < tok_end) ? t.v[jj][x] : 0u;
-    float c[4][EPL];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    if constexpr (FMT == kKvFp8) {
+      // byte e' of word x of tokens 2p and 2p + 1 side by side (one byte permute per two
+      // elements), then each pair converted at once: va[p] for element 4x + e'
 #pragma unroll
       for (int x = 0; x < VW; ++x) {
-        codes_to_f32<FMT, 0>(vw[jj][x], c[jj][4 * x], c[jj][4 * x + 1]);
-        codes_to_f32<FMT, 1>(vw[jj][x], c[jj][4 * x + 2], c[jj][4 * x + 3]);
-      }
+        unsigned lo[2], hi[2];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const u32x2 va = {pack16<DT>(c[0][e], c[1][e]), pack16<DT>(c[2][e], c[3][e])};
-      st.o[e] = mfma16<DT>(va, wb, st.o[e]);
+        for (int pr = 0; pr < 2; ++pr) {
+          lo[pr] = __builtin_amdgcn_perm(vw[2 * pr + 1][x], vw[2 * pr][x], 0x05010400u);
+          hi[pr] = __builtin_amdgcn_perm(vw[2 * pr + 1][x], vw[2 * pr][x], 0x07030602u);
+        }
+        const u32x2 v0 = {fp8_pair_bf16<0>(lo[0]), fp8_pair_bf16<0>(lo[1])};
+        const u32x2 v1 = {fp8_pair_bf16<1>(lo[0]), fp8_pair_bf16<1>(lo[1])};
+        const u32x2 v2 = {fp8_pair_bf16<0>(hi[0]), fp8_pair_bf16<0>(hi[1])};
+        const u32x2 v3 = {fp8_pair_bf16<1>(hi[0]), fp8_pair_bf16<1>(hi[1])};
+        st.o[4 * x] = mfma16<DT>(v0, wb, st.o[4 * x]);
+        st.o[4 * x + 1] = mfma16<DT>(v1, wb, st.o[4 * x + 1]);
+        st.o[4 * x + 2] = mfma16<DT>(v2, wb, st.o[4 * x + 2]);
+        st.o[4 * x + 3] = mfma16<DT>(v3, wb, st.o[4 * x + 3]);
+      }
+    } else {
+      float c[4][EPL];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int x = 0; x < VW; ++x) {
+          codes_to_f32<FMT, 0>(vw[jj][x], c[jj][4 * x], c[jj][4 * x + 1]);
+          codes_to_f32<FMT, 1>(vw[jj][x], c[jj][4 * x + 2], c[jj][4 * x + 3]);
+        }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const u32x2 va = {pack16<DT>(c[0][e], c[1][e]), pack16<DT>(c[2][e], c[3][e])};
+        st.o[e] = mfma16<DT>(va, wb, st.o[e]);
+      }
     }
   } else {
     // f16: the weights are rounded alone (an f16 product p s could fall below f16's range)
