@@ -349,12 +349,14 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
 // keeps one block in flight too, but without the drains and with the last blocks in a
 // loop of their own; the single-query kernels and the 8-bit kernels (one block ahead) and
 // the shared-prefix tasks (kPrefixDepth ahead) run faster with it, the multi-query kernels
-// do not and keep stream_tiles. `begin()` runs once, right after the first table entry's
-// load is issued.
+// do not and keep stream_tiles. `first_entry` is the table entry of block blk_begin, loaded
+// by the caller (the split kernel loads each segment's while the previous one streams, so
+// a segment's first tile is not waiting for a table load). `begin()` runs once, before the
+// first tile's load is issued.
 template <typename TileT, int kDepth, typename L, typename F, typename S>
 __device__ __forceinline__ void stream_tiles_pipelined(const DecodeArgs& a, int b, int blk_begin,
-                                                       int n_my, int& bad, L&& load,
-                                                       F&& process, S&& begin) {
+                                                       int n_my, int first_entry, int& bad,
+                                                       L&& load, F&& process, S&& begin) {
   const int32_t* trow = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_begin;
   auto entry = [&](int i) { return trow[min(i, n_my - 1)]; };   // same address in all lanes
   auto fetch = [&](TileT& t, int pb) {
@@ -369,7 +371,7 @@ __device__ __forceinline__ void stream_tiles_pipelined(const DecodeArgs& a, int 
   // Loads in the order of the loop body (entry of block d + 1, then tile d), so the loop is
   // entered with the same outstanding loads as it repeats with; a segment shorter than
   // kDepth blocks loads its last block again instead of skipping the load.
-  int e_next = entry(0);                    // table entry of the next block to fetch
+  int e_next = first_entry;                 // table entry of the next block to fetch
   begin();
 #pragma unroll
   for (int d0 = 0; d0 < kDepth; ++d0) {
@@ -412,8 +414,8 @@ struct NoBegin {
 template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true,
           bool kPipelined = false, typename F, typename S = NoBegin>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
-                                              int n_my, int lane, int& bad, F&& process,
-                                              S&& begin = S{}) {
+                                              int n_my, int first_entry, int lane, int& bad,
+                                              F&& process, S&& begin = S{}) {
   using G_ = Geo<DT, D>;
   const int r = lane >> 4, c = lane & 15;
   const uint32_t tok_stride = (uint32_t)a.n_kv_heads * G_::kRow;    // bytes between tokens
@@ -426,7 +428,8 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
                            a.v_pool + (size_t)pb * blk_stride, k_lane, v_lane, tok_stride);
   };
   if constexpr (kPipelined) {
-    stream_tiles_pipelined<Tile<DT, D>, kDepth>(a, b, blk_begin, n_my, bad, load, process, begin);
+    stream_tiles_pipelined<Tile<DT, D>, kDepth>(a, b, blk_begin, n_my, first_entry, bad, load,
+                                                process, begin);
   } else {
     begin();
     stream_tiles<Tile<DT, D>, kDepth>(a, b, blk_begin, n_my, lane, bad, load, process);
@@ -513,7 +516,7 @@ __device__ __forceinline__ void new_into_pool(const DecodeArgs& a, const u32x4* 
 template <int DT, int D, int G, bool kAppend>
 __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const DecodeArgs& a,
                                        int b, int j, int blk_begin, int n_my, int tok_end,
-                                       int n_ctx, int lane) {
+                                       int n_ctx, int first_entry, int lane) {
   const int r = lane >> 4, c = lane & 15;
   u32x4 qf[Geo<DT, D>::kNK];
   load_query<DT, D>(a, c < G, (size_t)b * a.n_heads + (size_t)j * G + c, r, qf);
@@ -529,7 +532,7 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
   }
   // the pipelined stream, one block ahead (two measured no faster, also for the private
   // blocks of the shared-prefix launch)
-  stream_blocks<DT, D, 1, true, true>(a, b, j, blk_begin, n_my, lane, bad,
+  stream_blocks<DT, D, 1, true, true>(a, b, j, blk_begin, n_my, first_entry, lane, bad,
                                       [&](Tile<DT, D>& t, int tok0) {
     if constexpr (kAppend)
       if (tok0 == new_tok0) new_into_tile<DT, D>(t, slot, t_new & (kBlockTokens - 1), lane);
@@ -790,7 +793,7 @@ __device__ __forceinline__ void attend_mq(MqState<DT, D>& st, int& bad, const De
     slot = sm_new[threadIdx.x >> 6];
     if (has_new) new_rows_to_lds_mq<DT, D, G>(a, b, j, lane, slot);
   }
-  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, lane, bad, [&](Tile<DT, D>& t, int tok0) {
+  stream_blocks<DT, D>(a, b, j, blk_begin, n_my, 0, lane, bad, [&](Tile<DT, D>& t, int tok0) {
     if constexpr (kAppend)
       if (has_new && tok0 + kBlockTokens > t0n) new_into_tile_mq<DT, D, G>(t, slot, tok0, t0n, a.q_len, lane);
     if (tok0 + kBlockTokens > lim_min)
@@ -1120,7 +1123,7 @@ __device__ __forceinline__ void process_block_q(QState<DT, D>& st, const QTile<D
 template <int DT, int D, int G, int FMT>
 __device__ __forceinline__ void attend_q(QState<DT, D>& st, int& bad, const DecodeArgs& a,
                                          int b, int j, int blk_begin, int n_my, int tok_end,
-                                         int lane) {
+                                         int first_entry, int lane) {
   const int r = lane >> 4, c = lane & 15;
   u32x4 qf[D / 32];
   float sumq;
@@ -1141,7 +1144,7 @@ __device__ __forceinline__ void attend_q(QState<DT, D>& st, int& bad, const Deco
   // scale registers per tile, INT8 147.4 -> 142.0 us and FP8 145.2 -> 139.8 us, the outputs
   // bitwise unchanged (two and three blocks ahead: 143.2 / 140.6 and 144.2 / 141.5 us).
   stream_tiles_pipelined<QTile<D>, 1>(
-      a, b, blk_begin, n_my, bad,
+      a, b, blk_begin, n_my, first_entry, bad,
       [&](QTile<D>& t, int pb) {
         const char* kb = kc + (size_t)pb * blk_stride;
         const char* vb = vc + (size_t)pb * blk_stride;
@@ -1241,12 +1244,12 @@ __device__ __forceinline__ void write_nan_rows(const DecodeArgs& a, size_t row0,
 template <int DT, int D, int G, int MODE, typename R>
 __device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, int blk_begin,
                                             int n_my, int tok_end, int n_ctx, bool whole,
-                                            int lane, R&& rec) {
+                                            int first_entry, int lane, R&& rec) {
   int bad = 0;
   if constexpr (MODE == kModeQuantInt8 || MODE == kModeQuantFp8) {
     QState<DT, D> st;
     attend_q<DT, D, G, MODE == kModeQuantInt8 ? kKvInt8 : kKvFp8>(st, bad, a, b, j, blk_begin,
-                                                                n_my, tok_end, lane);
+                                                                n_my, tok_end, first_entry, lane);
     st.l += __shfl_xor(st.l, 16);
     st.l += __shfl_xor(st.l, 32);
     if constexpr (MODE == kModeQuantInt8 && DT == 2) {     // O -= sum_t w_t z_t (column c)
@@ -1263,7 +1266,7 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, i
                        MODE == kModeSinglePrefix) {
     WaveState<DT, D, G> st;
     attend<DT, D, G, MODE == kModeSingleAppend>(st, bad, a, b, j, blk_begin, n_my, tok_end,
-                                                n_ctx, lane);
+                                                n_ctx, first_entry, lane);
     finish_rows<DT, D, G>(st);
     if (whole)
       write_final<DT, D, G>(a, st, bad, (size_t)b * a.n_heads + (size_t)j * G, lane);
@@ -1498,7 +1501,7 @@ __device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
   const int wph = a.prefix_wph;                 // 1, 2 or 4: divides NW
   const int heads_per_task = NW / wph;
   __shared__ int sm_members[kSplitMaxSeqs];
-  __shared__ int sm_flag[kSplitMaxSeqs];
+  __shared__ unsigned char sm_flag[kSplitMaxSeqs];
   __shared__ int sm_wsum[NW];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 4, c = lane & 15;
@@ -1597,7 +1600,8 @@ __device__ __forceinline__ void prefix_task(const DecodeArgs& a, int task) {
     // The waves of a KV head read the same blocks, so each keeps more of them in flight
     // than a decode wave does.
     stream_blocks<DT, D, kPrefixDepth<DT, D>, false, true>(a, leader, j, blk_begin,
-                                                           blk_end - blk_begin, lane, bad, proc);
+                                                           blk_end - blk_begin, lead_row[blk_begin],
+                                                           lane, bad, proc);
   }
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
@@ -1643,7 +1647,9 @@ __global__ __launch_bounds__(64 * NW) void decode_fixed_kernel(DecodeArgs a) {
   const int tok_end = min(n_ctx, (p + 1) * P);
   const int blk_begin = (p * P) >> 4;
   const int n_my = ((tok_end + 15) >> 4) - blk_begin;     // >= 1
-  run_segment<DT, D, G, MODE>(a, b, j, blk_begin, n_my, tok_end, n_ctx, n_part == 1, lane,
+  const int first_entry = a.block_tables[(size_t)b * a.max_blocks_per_seq + blk_begin];
+  run_segment<DT, D, G, MODE>(a, b, j, blk_begin, n_my, tok_end, n_ctx, n_part == 1,
+                            first_entry, lane,
                             [&](int c) { return mq_row<G>(a, b, j, c) * a.max_partitions + p; });
 }
 
@@ -1666,6 +1672,19 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   static_assert(kScanChunks <= 64, "one lane per chunk of 64 sequences");
   __shared__ int sm_pref[kSplitMaxSeqs + 1];   // blocks of sequences before b
   __shared__ int sm_chunk[kScanChunks];         // blocks of each chunk of 64 sequences
+  // The shared-prefix launch, whose short private parts make many segments, gets each
+  // segment's first table entry loaded while the previous segment streams, and reads a
+  // sequence's length from LDS: its tokens in its last block (1..16, stored minus one) and
+  // its shared blocks (plus kGroupedBit if it belongs to a group); the block counts give the
+  // rest. Measured on the 8 x 16-sequence shared-prefix batch (us warm / cold, same box):
+  // bf16 32 / 8 heads d 128 69.5 / 85.2 -> 68.4 / 84.1, d 64 50.4 / 59.4 -> 48.4 / 55.7,
+  // 64 / 8 heads 128.0 / 142.3 -> 125.2 / 140.2, fp32 78.1 / 94.0 -> 76.9 / 92.8. The other
+  // kernels, with one or two long segments per workgroup, load the entry at the segment's
+  // start: with the look-ahead the decode of the GQA batch measured 247.4 -> 248.2 us.
+  constexpr bool kEntryAhead = MODE == kModeSinglePrefix;
+  constexpr int kGroupedBit = 1 << 30;          // shared blocks are below 2^27
+  __shared__ unsigned char sm_last[kEntryAhead ? kSplitMaxSeqs : 1];
+  __shared__ int sm_skg[MODE == kModeSinglePrefix ? kSplitMaxSeqs : 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = a.num_seqs;
 
@@ -1686,7 +1705,11 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
     int nb = 0;
     if (s < B) {
       const int n = a.context_lens[s];
-      nb = usable(a, s, n) ? (n + kBlockTokens - 1) / kBlockTokens - shared_blocks_of(a, s, n) : 0;
+      const int skip = shared_blocks_of(a, s, n);
+      nb = valid_len(a, n) && skip >= 0 ? (n + kBlockTokens - 1) / kBlockTokens - skip : 0;
+      if constexpr (kEntryAhead) sm_last[s] = nb > 0 ? (n - 1) & (kBlockTokens - 1) : 0;
+      if constexpr (MODE == kModeSinglePrefix)
+        sm_skg[s] = nb > 0 ? skip | (a.seq_group[s] >= 0 ? kGroupedBit : 0) : 0;
     }
     const int incl = inclusive_scan(nb);
     if (s < B) sm_pref[s] = incl - nb;
@@ -1726,31 +1749,56 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(DecodeArgs a) {
   const int C = G * a.q_len;
   const long long u1 = sh.begin(w + 1);
   long long u = sh.begin(w);
-  while (u < u1) {
-    const int hg = (int)(u / T1);
-    const int rem = (int)(u - (long long)hg * T1);
+  // Unit x lies in stream (hg, b), at block blk0 of b's unshared blocks; the table entry of
+  // a segment's first block is loaded while the previous segment streams.
+  struct Where { int hg, b, blk0, skg; };
+  auto locate = [&](long long x) {
+    Where p;
+    p.hg = (int)(x / T1);
+    const int rem = (int)(x - (long long)p.hg * T1);
     int lo = 0, hi = B;                         // last b with sm_pref[b] <= rem
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (sm_pref[mid] <= rem) lo = mid; else hi = mid;
     }
-    const int b = lo;
-    const int n_ctx = a.context_lens[b];
-    const int skip = shared_blocks_of(a, b, n_ctx);   // >= 0: b has units
-    const int blk0 = rem - sm_pref[b];                // within the unshared blocks
+    p.b = __builtin_amdgcn_readfirstlane(lo);                      // uniform
+    p.blk0 = __builtin_amdgcn_readfirstlane(rem - sm_pref[p.b]);
+    p.skg = 0;
+    if constexpr (MODE == kModeSinglePrefix) p.skg = __builtin_amdgcn_readfirstlane(sm_skg[p.b]);
+    return p;
+  };
+  auto first_entry_of = [&](const Where& p) {
+    return a.block_tables[(size_t)p.b * a.max_blocks_per_seq + (p.skg & (kGroupedBit - 1)) + p.blk0];
+  };
+  Where cur = locate(u);
+  int e_cur = kEntryAhead && u < u1 ? first_entry_of(cur) : 0;
+  while (u < u1) {
+    if constexpr (!kEntryAhead) e_cur = first_entry_of(cur);    // unused by multi-query
+    const int hg = cur.hg, b = cur.b, blk0 = cur.blk0;
+    const int skip = cur.skg & (kGroupedBit - 1);     // b's shared blocks (0 ungrouped)
     const int nb = sm_pref[b + 1] - sm_pref[b];
+    const int n_ctx = kEntryAhead ? (skip + nb - 1) * kBlockTokens + sm_last[b] + 1
+                                  : a.context_lens[b];
     const long long seg_end = min(u1, (long long)hg * T1 + sm_pref[b + 1]);
     const int n_my = (int)(seg_end - u);
+    Where nxt = cur;
+    int e_nxt = 0;
+    if (kEntryAhead && seg_end < u1) {
+      nxt = locate(seg_end);
+      e_nxt = first_entry_of(nxt);
+    }
     const int j = hg * NW + wave;
     if (j < a.n_kv_heads) {
       const int tok_end = min(n_ctx, (skip + blk0 + n_my) * kBlockTokens);
       const size_t rec0 = ((size_t)(w + (long long)hg * B + b) * NW + wave) * C;
       // a sequence with a shared prefix always leaves a record: the merge adds the prefix
       run_segment<DT, D, G, MODE>(a, b, j, skip + blk0, n_my, tok_end, n_ctx,
-                                skip == 0 && blk0 == 0 && n_my == nb && !(a.seq_group && a.seq_group[b] >= 0),
-                                lane, [&](int c) { return rec0 + c; });
+                                skip == 0 && blk0 == 0 && n_my == nb && !(cur.skg & kGroupedBit),
+                                e_cur, lane, [&](int c) { return rec0 + c; });
     }
     u = seg_end;
+    cur = kEntryAhead || u >= u1 ? nxt : locate(u);
+    e_cur = e_nxt;
   }
 }
 
