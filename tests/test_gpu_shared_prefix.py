@@ -177,6 +177,31 @@ def test_member_with_a_different_table_gets_nan():
     assert_close(got[keep], oracle_out(wl)[keep], "bf16", "others")
 
 
+def test_out_of_pool_entries_give_nan_for_their_sequences():
+    """Table entries past the pool: one in the first member's shared run (read by the prefix
+    tasks, here four waves per KV head staging blocks through LDS) makes the whole group NaN;
+    one at the first private block of a sequence in another group (the entry the split
+    kernel loads a segment ahead) makes that sequence NaN. Nothing outside the pool is
+    read, and every other output matches the oracle."""
+    _log("shared prefix: out-of-pool table entries")
+    wl = sp_workload(B=24, groups=2, prefix=300, suffix=(20, 90), seed=21)
+    grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
+    assert grp.n_groups == 2 and (grp.max_group_size * 4 + 15) // 16 >= 3   # 4 waves per head
+    t = wlm.to_torch(wl, DEV)
+    pkv.pkv_kv_append(t["k_pool"], t["v_pool"], t["k_new"], t["v_new"], t["block_tables"],
+                      t["positions"])
+    g0 = np.flatnonzero(grp.seq_group == 0)
+    g1 = np.flatnonzero(grp.seq_group == 1)
+    t["block_tables"][int(g0[0]), 1] = wl.num_blocks + 5     # inside group 0's shared run
+    victim = int(g1[3])
+    t["block_tables"][victim, int(grp.group_blocks[1])] = wl.num_blocks + 9   # first private
+    got, _ = gpu_shared(wl, grp, t=t)
+    assert np.isnan(got[g0]).all()
+    assert np.isnan(got[victim]).all()
+    keep = [b for b in range(wl.batch) if b not in set(g0.tolist()) | {victim}]
+    assert_close(got[keep], oracle_out(wl)[keep], "bf16", "others")
+
+
 def test_invalid_groups_give_nan_for_their_members_only():
     wl = sp_workload(B=12, groups=3, prefix=120, seed=8)
     grp = find_shared_prefixes(wl.block_tables, wl.context_lens)
