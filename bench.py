@@ -14,8 +14,11 @@ Prints ONE JSON line: the metric is KV GB/s read (whole step), with the decode l
 achieved bandwidth against the 8 TB/s HBM peak in "roofline", and the fp64 CPU oracle timed
 on a bounded sample of the same workload in "cpu_baseline".
 
-    python bench.py [--steps K] [--warmup W] [--config 3] [--partition 0] [--all]
-                    [--separate-append]
+The default line times the GQA bf16 layer (workload 3) and, in the same run, the
+long-context GQA layer (workload 4), summarised under "also_measured".
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--also 4] [--partition 0]
+                    [--all] [--separate-append]
 """
 
 from __future__ import annotations
@@ -77,7 +80,7 @@ def measured_traffic(*key):
     return entry["bytes"] if decode_source_sha() == entry["decode_source_sha256"] else None
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
@@ -89,6 +92,10 @@ def parse():
     ap.add_argument("--config", type=int, default=3,
                     help="workload id 1..5 (default 3, the GQA bf16 layer: 64 sequences of "
                          "4096-8192 tokens, the largest workload that the step reads)")
+    ap.add_argument("--also", type=str, default=None, metavar="IDS",
+                    help="comma-separated workload ids timed in the same run after --config and "
+                         "summarised under also_measured in its line (default: 4, the "
+                         "long-context GQA layer, when --config is 3; '' for none)")
     ap.add_argument("--partition", type=int, default=0,
                     help="tokens per KV partition; 0 = the library's balanced split")
     ap.add_argument("--all", action="store_true", help="one line per workload 1..5")
@@ -113,7 +120,7 @@ def parse():
     ap.add_argument("--q-len", type=int, default=4, help="new tokens per sequence (multi-query)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time for the oracle sample")
-    args = ap.parse_args()
+    args = ap.parse_args(argv)
     gpu_steps = args.component != "block-manager"
     if args.steps is None:
         args.steps = 200 if gpu_steps else 50
@@ -886,7 +893,38 @@ def main():
     cfgs = [1, 2, 3, 4, 5] if args.all else [args.config]
     for cfg in cfgs:
         res = run_config(args, cfg, want_cpu=not args.no_cpu_baseline)
+        if not args.all:
+            also = also_workloads(args)
+            if also:
+                res["also_measured"] = [also_summary(run_config(args, c, want_cpu=False))
+                                        for c in also]
         print(json.dumps(res), flush=True)
+
+
+def also_workloads(args) -> list:
+    """Workloads timed after the main one in the same line: --also, else the long-context
+    GQA layer (4) beside the GQA layer (3)."""
+    if args.also is None:
+        return [4] if args.config == 3 else []
+    ids = [int(x) for x in args.also.split(",") if x.strip()]
+    bad = [i for i in ids if i not in (1, 2, 3, 4, 5)]
+    if bad:
+        raise SystemExit(f"--also: unknown workload ids {bad}")
+    return [i for i in ids if i != args.config]
+
+
+def also_summary(res: dict) -> dict:
+    """The figures of a secondary workload's line, timed the same way as the main one."""
+    keys = ("value", "unit", "us_per_step", "pct_of_hbm_peak", "dtype", "steps", "warmup")
+    out = {"workload": res["config"]["workload"]}
+    out.update({k: res[k] for k in keys})
+    out["config"] = res["config"]
+    out["roofline"] = res["roofline"]
+    out["ceiling"] = res["ceiling"]
+    out["timing"] = {k: res["timing"][k] for k in ("step_us_median", "decode_kv_gbps",
+                                                     "separate_step_us")
+                     if k in res["timing"]}
+    return out
 
 
 if __name__ == "__main__":

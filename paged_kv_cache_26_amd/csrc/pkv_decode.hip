@@ -352,8 +352,12 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, int b, int blk
 // do not and keep stream_tiles. `first_entry` is the table entry of block blk_begin, loaded
 // by the caller (the split kernel loads each segment's while the previous one streams, so
 // a segment's first tile is not waiting for a table load). `begin()` runs once, before the
-// first tile's load is issued.
-template <typename TileT, int kDepth, typename L, typename F, typename S>
+// first tile's load is issued. With kEntryRing the table entries go through a ring of NB
+// registers instead, each loaded a whole unroll group (NB iterations) before its fetch, so
+// waiting for an entry never waits for the tiles issued after it either; the private
+// segments of the shared-prefix launch stream two blocks ahead this way.
+template <typename TileT, int kDepth, bool kEntryRing = false, typename L, typename F,
+          typename S>
 __device__ __forceinline__ void stream_tiles_pipelined(const DecodeArgs& a, int b, int blk_begin,
                                                        int n_my, int first_entry, int& bad,
                                                        L&& load, F&& process, S&& begin) {
@@ -368,6 +372,38 @@ __device__ __forceinline__ void stream_tiles_pipelined(const DecodeArgs& a, int 
 
   constexpr int NB = kDepth + 1;
   TileT tt[NB];
+  if constexpr (kEntryRing) {
+    // before iteration i, ent[i % NB] holds the entry of block i + kDepth (the block that
+    // iteration fetches); block i's tile is tt[i % NB]
+    int ent[NB];
+    begin();
+#pragma unroll
+    for (int u = 0; u < NB; ++u) ent[u] = entry(kDepth + u);
+#pragma unroll
+    for (int d0 = 0; d0 < kDepth; ++d0) fetch(tt[d0], d0 == 0 ? first_entry : entry(d0));
+    const int n_fetching = n_my - kDepth;
+    int i0 = 0;
+    for (; i0 + NB <= n_fetching; i0 += NB) {
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = i0 + u;
+        const int pb = ent[u];
+        ent[u] = entry(i + kDepth + NB);
+        fetch(tt[(u + kDepth) % NB], pb);
+        process(tt[u], (blk_begin + i) * kBlockTokens);
+      }
+    }
+    for (; i0 < n_my; i0 += NB) {            // at most NB + kDepth - 1 blocks, no refills
+#pragma unroll
+      for (int u = 0; u < NB; ++u) {
+        const int i = i0 + u;
+        if (i >= n_my) break;
+        if (i < n_fetching) fetch(tt[(u + kDepth) % NB], ent[u]);
+        process(tt[u], (blk_begin + i) * kBlockTokens);
+      }
+    }
+    return;
+  }
   // Loads in the order of the loop body (entry of block d + 1, then tile d), so the loop is
   // entered with the same outstanding loads as it repeats with; a segment shorter than
   // kDepth blocks loads its last block again instead of skipping the load.
@@ -412,7 +448,7 @@ struct NoBegin {
 };
 
 template <int DT, int D, int kDepth = Geo<DT, D>::kDepth, bool NT_V = true,
-          bool kPipelined = false, typename F, typename S = NoBegin>
+          bool kPipelined = false, bool kEntryRing = false, typename F, typename S = NoBegin>
 __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j, int blk_begin,
                                               int n_my, int first_entry, int lane, int& bad,
                                               F&& process, S&& begin = S{}) {
@@ -428,8 +464,8 @@ __device__ __forceinline__ void stream_blocks(const DecodeArgs& a, int b, int j,
                            a.v_pool + (size_t)pb * blk_stride, k_lane, v_lane, tok_stride);
   };
   if constexpr (kPipelined) {
-    stream_tiles_pipelined<Tile<DT, D>, kDepth>(a, b, blk_begin, n_my, first_entry, bad, load,
-                                                process, begin);
+    stream_tiles_pipelined<Tile<DT, D>, kDepth, kEntryRing>(a, b, blk_begin, n_my, first_entry,
+                                                            bad, load, process, begin);
   } else {
     begin();
     stream_tiles<Tile<DT, D>, kDepth>(a, b, blk_begin, n_my, lane, bad, load, process);
@@ -513,7 +549,7 @@ __device__ __forceinline__ void new_into_pool(const DecodeArgs& a, const u32x4* 
   *reinterpret_cast<u32x4*>(pool + dst) = slot[lane];
 }
 
-template <int DT, int D, int G, bool kAppend>
+template <int DT, int D, int G, bool kAppend, bool kTwoAhead = false>
 __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const DecodeArgs& a,
                                        int b, int j, int blk_begin, int n_my, int tok_end,
                                        int n_ctx, int first_entry, int lane) {
@@ -530,10 +566,11 @@ __device__ __forceinline__ void attend(WaveState<DT, D, G>& st, int& bad, const 
     slot = sm_new[threadIdx.x >> 6];
     if (has_new) piece = new_rows_load<DT, D>(a, b, j, lane);
   }
-  // the pipelined stream, one block ahead (two measured no faster, also for the private
-  // blocks of the shared-prefix launch)
-  stream_blocks<DT, D, 1, true, true>(a, b, j, blk_begin, n_my, first_entry, lane, bad,
-                                      [&](Tile<DT, D>& t, int tok0) {
+  // the pipelined stream one block ahead (two measured no faster); kTwoAhead: two blocks
+  // ahead with the table entries in a ring (the shared-prefix launch's private segments,
+  // which are short, so a wave starts many of them)
+  stream_blocks<DT, D, kTwoAhead ? 2 : 1, true, true, kTwoAhead>(
+      a, b, j, blk_begin, n_my, first_entry, lane, bad, [&](Tile<DT, D>& t, int tok0) {
     if constexpr (kAppend)
       if (tok0 == new_tok0) new_into_tile<DT, D>(t, slot, t_new & (kBlockTokens - 1), lane);
     // only the last block of a sequence can be partial (partitions are block aligned)
@@ -1265,8 +1302,8 @@ __device__ __forceinline__ void run_segment(const DecodeArgs& a, int b, int j, i
   } else if constexpr (MODE == kModeSingle || MODE == kModeSingleAppend ||
                        MODE == kModeSinglePrefix) {
     WaveState<DT, D, G> st;
-    attend<DT, D, G, MODE == kModeSingleAppend>(st, bad, a, b, j, blk_begin, n_my, tok_end,
-                                                n_ctx, first_entry, lane);
+    attend<DT, D, G, MODE == kModeSingleAppend, MODE == kModeSinglePrefix>(
+        st, bad, a, b, j, blk_begin, n_my, tok_end, n_ctx, first_entry, lane);
     finish_rows<DT, D, G>(st);
     if (whole)
       write_final<DT, D, G>(a, st, bad, (size_t)b * a.n_heads + (size_t)j * G, lane);

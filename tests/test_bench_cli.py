@@ -34,3 +34,11 @@ def test_measured_traffic_is_dropped_when_the_kernel_source_changes(monkeypatch)
                         {"bytes": 123, "decode_source_sha256": "0" * 16})
     assert bench.measured_traffic(9, 0, True) is None
     assert bench.measured_traffic(9, 64, True) is None
+
+
+def test_default_line_also_times_the_long_context_workload():
+    args = bench.parse([])
+    assert args.config == 3 and bench.also_workloads(args) == [4]
+    assert bench.also_workloads(bench.parse(["--config", "2"])) == []
+    assert bench.also_workloads(bench.parse(["--also", ""])) == []
+    assert bench.also_workloads(bench.parse(["--also", "3,5"])) == [5]
