@@ -697,15 +697,13 @@ __device__ __forceinline__ void process_block_mq(MqState<DT, D>& st, const Tile<
     }
 #pragma unroll
     for (int e = 0; e < G_::kEPL; ++e) {
+      // one byte permute per word: {tokens 4r+1, 4r} and {4r+3, 4r+2} of element e
+      // (v_perm_b32 selects from {S0, S1}: bytes 0-3 are S1's, 4-7 S0's)
       const int x = e >> 1;
+      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;   // high or low halves
       u32x2 va;
-      if (e & 1) {      // high halves of the four tokens' word x
-        va[0] = (w[1][x] & 0xFFFF0000u) | (w[0][x] >> 16);
-        va[1] = (w[3][x] & 0xFFFF0000u) | (w[2][x] >> 16);
-      } else {          // low halves
-        va[0] = (w[1][x] << 16) | (w[0][x] & 0xFFFFu);
-        va[1] = (w[3][x] << 16) | (w[2][x] & 0xFFFFu);
-      }
+      va[0] = __builtin_amdgcn_perm(w[1][x], w[0][x], sel);
+      va[1] = __builtin_amdgcn_perm(w[3][x], w[2][x], sel);
       if constexpr (DT == 2) {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         st.o[e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
