@@ -48,16 +48,16 @@ HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 # then pkv_internal.h with the launch constants); it is reported only while those sources
 # are unchanged.
 MEASURED_TRAFFIC = {
-    (3, 0, True): {"bytes": 1587493072, "decode_source_sha256": "d47fd8625a8e12f4"},
-    (3, 0, False): {"bytes": 1586989274, "decode_source_sha256": "d47fd8625a8e12f4"},
-    (4, 0, True): {"bytes": 1352645046, "decode_source_sha256": "d47fd8625a8e12f4"},
-    (4, 0, False): {"bytes": 1352603199, "decode_source_sha256": "d47fd8625a8e12f4"},
-    (2, 0, True): {"bytes": 1194501486, "decode_source_sha256": "d47fd8625a8e12f4"},
-    (2, 0, False): {"bytes": 1193385036, "decode_source_sha256": "d47fd8625a8e12f4"},
-    ("multi-query", 4): {"bytes": 1628049541, "decode_source_sha256": "d47fd8625a8e12f4"},
-    ("shared-prefix",): {"bytes": 389833954, "decode_source_sha256": "d47fd8625a8e12f4"},
-    ("quantized", "int8"): {"bytes": 849910946, "decode_source_sha256": "d47fd8625a8e12f4"},
-    ("quantized", "fp8"): {"bytes": 849764727, "decode_source_sha256": "d47fd8625a8e12f4"},
+    (3, 0, True): {"bytes": 1587575569, "decode_source_sha256": "7d0c5f462cc26f68"},
+    (3, 0, False): {"bytes": 1586996592, "decode_source_sha256": "7d0c5f462cc26f68"},
+    (4, 0, True): {"bytes": 1352698833, "decode_source_sha256": "7d0c5f462cc26f68"},
+    (4, 0, False): {"bytes": 1352623975, "decode_source_sha256": "7d0c5f462cc26f68"},
+    (2, 0, True): {"bytes": 1194508606, "decode_source_sha256": "7d0c5f462cc26f68"},
+    (2, 0, False): {"bytes": 1193405791, "decode_source_sha256": "7d0c5f462cc26f68"},
+    ("multi-query", 4): {"bytes": 1628098490, "decode_source_sha256": "7d0c5f462cc26f68"},
+    ("shared-prefix",): {"bytes": 390049623, "decode_source_sha256": "7d0c5f462cc26f68"},
+    ("quantized", "int8"): {"bytes": 849889453, "decode_source_sha256": "7d0c5f462cc26f68"},
+    ("quantized", "fp8"): {"bytes": 849799654, "decode_source_sha256": "7d0c5f462cc26f68"},
 }
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_26_amd", "csrc", name)
                   for name in ("pkv_decode.hip", "pkv_internal.h")]
