@@ -124,8 +124,13 @@ def _ptr(t: torch.Tensor | None) -> int | None:
 
 
 def _stream(stream) -> int:
+    """The stream's handle; a given stream must belong to the current device, where the
+    tensors are (_check_device) and where the library launches."""
     if stream is None:
         stream = torch.cuda.current_stream()
+    else:
+        _require(stream.device == torch.device("cuda", torch.cuda.current_device()),
+                 "stream must belong to the current device")
     return stream.cuda_stream
 
 
@@ -135,11 +140,16 @@ def _require(cond: bool, msg: str) -> None:
 
 
 def _check_device(*tensors: torch.Tensor) -> None:
-    """Every tensor on the GPU, contiguous, and all on the same device."""
+    """Every tensor on the GPU, contiguous, and all on the current device (the library
+    launches its kernels there)."""
     for t in tensors:
         _require(t.is_cuda, "tensors must be on the GPU")
         _require(t.is_contiguous(), "tensors must be contiguous")
-    _require(len({t.device for t in tensors}) <= 1, "tensors must be on the same device")
+    devices = {t.device for t in tensors}
+    _require(len(devices) <= 1, "tensors must be on the same device")
+    if devices:
+        _require(next(iter(devices)).index == torch.cuda.current_device(),
+                 "tensors must be on the current device (torch.cuda.set_device)")
 
 
 def _opt(t):
@@ -537,7 +547,9 @@ def pkv_stream_read(buf, sink, workgroups: int = 0, nbytes: int | None = None,
     lib = load_library()
     _require(sink.dtype == torch.int32 or sink.dtype == torch.uint32, "sink must be 32-bit")
     _check_device(buf, sink)
-    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    size = buf.numel() * buf.element_size()
+    n = size if nbytes is None else int(nbytes)
+    _require(0 < n <= size, "nbytes must lie in (0, the buffer's size]")
     st = lib.pkv_stream_read(_ptr(buf), n, _ptr(sink), sink.numel(), int(workgroups),
                              _stream(stream))
     if st != 0:

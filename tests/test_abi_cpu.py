@@ -344,3 +344,15 @@ def test_noalloc_step_rejects_sizes_beyond_its_scratch_on_host(lib):
     bad = list(args)
     bad[8], bad[15] = 4, 96                   # a small batch with an unsupported head size
     assert f(*bad) == -4
+
+
+def test_stream_read_binding_bounds_nbytes_by_the_buffer(lib, monkeypatch):
+    """nbytes beyond the buffer would read past it: refused before any launch (the device
+    check is bypassed so that the size check runs without a GPU)."""
+    import torch
+    monkeypatch.setattr(pkv, "_check_device", lambda *t: None)
+    buf = torch.zeros(64, dtype=torch.int32)
+    sink = torch.zeros(256, dtype=torch.int32)
+    for n in (0, 257, 1 << 20):
+        with pytest.raises(ValueError, match="nbytes"):
+            pkv.pkv_stream_read(buf, sink, nbytes=n)
